@@ -1,0 +1,207 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 CPU oracle for block-sparse masked FlexAttention forward.
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it.  The product path (the HIP library) never calls it, and this
+ * file shares no code, header or constant with that library.
+ *
+ * What it computes, and where each piece comes from:
+ *
+ *  - Element masks (mask_true).  "[Inductor][Flex Attention] Add Subtiling
+ *    Option for Alpha Scaling" names the mask_mod hook and the sliding-window
+ *    use case (Summary); "Performance for templated attention strangely bad
+ *    for a combination of causal + upper square mask" spells out the
+ *    prefix-bidirectional-or-causal predicate with an inclusive bound of 1024
+ *    and masked scores set to -inf (the bad.py -> bad2.py diff).  Causal is
+ *    the q >= kv half of that same predicate.  The sliding window is the
+ *    causal predicate further limited to q - kv <= window; window_min is an
+ *    extra lower bound on q - kv (0 for the plain causal window).
+ *
+ *  - Scores.  s = scale * <q_i, k_j> from the exact input values widened to
+ *    fp64, then the score modification is applied to the scaled score.  The
+ *    identity modification leaves it alone; the relative-position bias
+ *    subtracts slope_h * (i - j), slope_h = 2^(-bias_max * (h + 1) / H).
+ *
+ *  - Softmax.  The online-softmax recurrence of forward_block_mn (the
+ *    common.py.jinja hunk: running max, alpha rescale of the accumulator and
+ *    of the row sum l_i) has the ordinary softmax as its fixed point, so the
+ *    oracle is that definition written out densely: over every visible key,
+ *    w_j = exp(s_j - max), out = sum_j w_j v_j / sum_j w_j,
+ *    lse = max + ln(sum_j w_j).  A row that sees no key returns out = 0 and
+ *    lse = -inf (the guarded case ROWS_GUARANTEED_SAFE=False leaves on).
+ *
+ *  - Block arrays (oracle_block_mask).  Brute force: every element of every
+ *    Q_BLOCK x KV_BLOCK tile is evaluated; positions beyond q_len / kv_len
+ *    count as masked.  A tile with every element visible is "full", one with
+ *    some is "partial", one with none is skipped.  Each row of kv_indices
+ *    (resp. full_kv_indices) lists its partial (resp. full) kv-blocks in
+ *    ascending order, followed by every remaining kv-block in ascending
+ *    order, so each row is a permutation of 0..n_kv_blocks-1.  The field
+ *    names come from the block-mask tuple of the flex_attention
+ *    higher-order-op call in the test hunks of the subtiling page.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MASK_NOOP 0
+#define ORACLE_MASK_CAUSAL 1
+#define ORACLE_MASK_SLIDING_WINDOW 2
+#define ORACLE_MASK_PREFIX_CAUSAL 3
+
+#define ORACLE_SCORE_IDENTITY 0
+#define ORACLE_SCORE_REL_BIAS 1
+
+/* Is key j visible from query i?  Positions out of range are never visible. */
+static int mask_true(int kind, int64_t window, int64_t window_min,
+                     int64_t prefix, int64_t i, int64_t j, int64_t q_len,
+                     int64_t kv_len) {
+  if (i < 0 || j < 0 || i >= q_len || j >= kv_len) return 0;
+  switch (kind) {
+    case ORACLE_MASK_NOOP:
+      return 1;
+    case ORACLE_MASK_CAUSAL:
+      return i >= j;
+    case ORACLE_MASK_SLIDING_WINDOW:
+      return (i - j >= window_min) && (i - j <= window);
+    case ORACLE_MASK_PREFIX_CAUSAL:
+      return ((i <= prefix) && (j <= prefix)) || (i >= j);
+    default:
+      return -1;
+  }
+}
+
+int oracle_mask_value(int kind, int64_t window, int64_t window_min,
+                      int64_t prefix, int64_t i, int64_t j, int64_t q_len,
+                      int64_t kv_len) {
+  return mask_true(kind, window, window_min, prefix, i, j, q_len, kv_len);
+}
+
+/* Number of visible (i, j) pairs over the whole q_len x kv_len square. */
+int64_t oracle_count_visible(int kind, int64_t window, int64_t window_min,
+                             int64_t prefix, int64_t q_len, int64_t kv_len) {
+  int64_t n = 0;
+  for (int64_t i = 0; i < q_len; ++i)
+    for (int64_t j = 0; j < kv_len; ++j)
+      n += mask_true(kind, window, window_min, prefix, i, j, q_len, kv_len) == 1;
+  return n;
+}
+
+/* Brute-force block arrays.  Returns 0, or -1 on a bad argument. */
+int oracle_block_mask(int kind, int64_t window, int64_t window_min,
+                      int64_t prefix, int64_t q_len, int64_t kv_len,
+                      int64_t q_block, int64_t kv_block, int32_t* kv_num_blocks,
+                      int32_t* kv_indices, int32_t* full_kv_num_blocks,
+                      int32_t* full_kv_indices) {
+  if (kind < 0 || kind > 3 || q_len < 0 || kv_len < 0 || q_block <= 0 ||
+      kv_block <= 0)
+    return -1;
+  int64_t nq = (q_len + q_block - 1) / q_block;
+  int64_t nk = (kv_len + kv_block - 1) / kv_block;
+  /* tile class: 0 empty, 1 partial, 2 full */
+  int* cls = (int*)malloc(sizeof(int) * (size_t)(nk > 0 ? nk : 1));
+  if (!cls) return -1;
+  for (int64_t qb = 0; qb < nq; ++qb) {
+    for (int64_t kb = 0; kb < nk; ++kb) {
+      int64_t count = 0;
+      for (int64_t i = qb * q_block; i < (qb + 1) * q_block; ++i)
+        for (int64_t j = kb * kv_block; j < (kb + 1) * kv_block; ++j)
+          count += mask_true(kind, window, window_min, prefix, i, j, q_len,
+                             kv_len) == 1;
+      cls[kb] = count == 0 ? 0 : (count == q_block * kv_block ? 2 : 1);
+    }
+    for (int want = 1; want <= 2; ++want) {
+      int32_t* num = want == 1 ? kv_num_blocks : full_kv_num_blocks;
+      int32_t* idx = (want == 1 ? kv_indices : full_kv_indices) + qb * nk;
+      int64_t w = 0;
+      for (int64_t kb = 0; kb < nk; ++kb)
+        if (cls[kb] == want) idx[w++] = (int32_t)kb;
+      num[qb] = (int32_t)w;
+      for (int64_t kb = 0; kb < nk; ++kb)
+        if (cls[kb] != want) idx[w++] = (int32_t)kb;
+    }
+  }
+  free(cls);
+  return 0;
+}
+
+/*
+ * Attention for a list of query rows.  q is [B, H, q_len, d], k is
+ * [B, H, kv_len, d], v is [B, H, kv_len, dv], all contiguous float32 holding
+ * the exact input values.  rows[r] is the flat row id (b * H + h) * q_len + i.
+ * Writes out[r * dv + c] and lse[r] in fp64.  Returns 0, or -1 on a bad
+ * argument or allocation failure.
+ */
+int oracle_attention_rows(const float* q, const float* k, const float* v,
+                          int64_t B, int64_t H, int64_t q_len, int64_t kv_len,
+                          int64_t d, int64_t dv, int mask_kind, int64_t window,
+                          int64_t window_min, int64_t prefix, int score_kind,
+                          double bias_max, double scale, const int64_t* rows,
+                          int64_t n_rows, double* out, double* lse) {
+  if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
+    return -1;
+  if (mask_kind < 0 || mask_kind > 3) return -1;
+  if (score_kind != ORACLE_SCORE_IDENTITY && score_kind != ORACLE_SCORE_REL_BIAS)
+    return -1;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
+  double* acc = (double*)malloc(sizeof(double) * (size_t)dv);
+  if (!s || !acc) {
+    free(s);
+    free(acc);
+    return -1;
+  }
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int64_t id = rows[r];
+    if (id < 0 || id >= B * H * q_len) {
+      free(s);
+      free(acc);
+      return -1;
+    }
+    int64_t bh = id / q_len, i = id % q_len, h = bh % H;
+    const float* qi = q + id * d;
+    const float* kb = k + bh * kv_len * d;
+    const float* vb = v + bh * kv_len * dv;
+    double slope = pow(2.0, -bias_max * (double)(h + 1) / (double)H);
+
+    /* scores for every key; masked ones are -inf */
+    double mx = -INFINITY;
+    int any = 0;
+    for (int64_t j = 0; j < kv_len; ++j) {
+      if (mask_true(mask_kind, window, window_min, prefix, i, j, q_len,
+                    kv_len) != 1) {
+        s[j] = -INFINITY;
+        continue;
+      }
+      double dot = 0.0;
+      for (int64_t c = 0; c < d; ++c)
+        dot += (double)qi[c] * (double)kb[j * d + c];
+      double sj = scale * dot;
+      if (score_kind == ORACLE_SCORE_REL_BIAS) sj -= slope * (double)(i - j);
+      s[j] = sj;
+      if (sj > mx) mx = sj;
+      any = 1;
+    }
+
+    double* o = out + r * dv;
+    if (!any) {
+      for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double l = 0.0;
+    for (int64_t c = 0; c < dv; ++c) acc[c] = 0.0;
+    for (int64_t j = 0; j < kv_len; ++j) {
+      if (s[j] == -INFINITY) continue;
+      double w = exp(s[j] - mx);
+      l += w;
+      for (int64_t c = 0; c < dv; ++c) acc[c] += w * (double)vb[j * dv + c];
+    }
+    for (int64_t c = 0; c < dv; ++c) o[c] = acc[c] / l;
+    lse[r] = mx + log(l);
+  }
+  free(s);
+  free(acc);
+  return 0;
+}

@@ -1,0 +1,177 @@
+"""Python side of the fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product path never does, and this
+module imports nothing from the product package.
+
+``oracle.c`` holds the arithmetic (see its header for the passages each part
+follows).  This wrapper only compiles it with gcc, marshals numpy arrays and
+spreads independent query rows over host threads (each row is computed by the
+same plain C loop; splitting rows changes no arithmetic).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
+
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3}
+SCORE_KINDS = {"identity": 0, "rel_bias": 1}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into a shared library with gcc; returns its path."""
+    os.makedirs(_OUT_DIR, exist_ok=True)
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, i32p, f32p, f64p, i64p = (
+            ctypes.c_int64,
+            ctypes.POINTER(ctypes.c_int32),
+            ctypes.POINTER(ctypes.c_float),
+            ctypes.POINTER(ctypes.c_double),
+            ctypes.POINTER(ctypes.c_int64),
+        )
+        lib.oracle_mask_value.argtypes = [ctypes.c_int] + [i64] * 7
+        lib.oracle_mask_value.restype = ctypes.c_int
+        lib.oracle_count_visible.argtypes = [ctypes.c_int] + [i64] * 5
+        lib.oracle_count_visible.restype = i64
+        lib.oracle_block_mask.argtypes = [ctypes.c_int] + [i64] * 7 + [i32p] * 4
+        lib.oracle_block_mask.restype = ctypes.c_int
+        lib.oracle_attention_rows.argtypes = (
+            [f32p, f32p, f32p] + [i64] * 6 + [ctypes.c_int, i64, i64, i64]
+            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p]
+        )
+        lib.oracle_attention_rows.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _mask_args(mask: dict):
+    kind = MASK_KINDS[mask["kind"]]
+    return (
+        kind,
+        int(mask.get("window", 0)),
+        int(mask.get("window_min", 0)),
+        int(mask.get("prefix", 0)),
+    )
+
+
+def mask_value(mask: dict, i: int, j: int, q_len: int, kv_len: int) -> bool:
+    r = _load().oracle_mask_value(*_mask_args(mask), i, j, q_len, kv_len)
+    if r < 0:
+        raise ValueError("bad mask")
+    return bool(r)
+
+
+def count_visible(mask: dict, q_len: int, kv_len: int) -> int:
+    return int(_load().oracle_count_visible(*_mask_args(mask), q_len, kv_len))
+
+
+def block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int):
+    """Brute-force block arrays: (kv_num_blocks, kv_indices, full_kv_num_blocks,
+    full_kv_indices) as int32 numpy arrays of shapes [nQB], [nQB, nKVB]."""
+    nq = -(-q_len // q_block)
+    nk = -(-kv_len // kv_block)
+    arrs = [
+        np.zeros(nq, np.int32),
+        np.zeros((nq, nk), np.int32),
+        np.zeros(nq, np.int32),
+        np.zeros((nq, nk), np.int32),
+    ]
+    ptrs = [a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for a in arrs]
+    r = _load().oracle_block_mask(
+        *_mask_args(mask), q_len, kv_len, q_block, kv_block, *ptrs
+    )
+    if r != 0:
+        raise ValueError("oracle_block_mask rejected its arguments")
+    return tuple(arrs)
+
+
+def _cpu_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
+                   threads: int | None = None):
+    """fp64 attention for selected rows.
+
+    q: [B, H, Lq, D], k: [B, H, Lkv, D], v: [B, H, Lkv, Dv] float32 arrays (or
+    anything numpy turns into float32 without changing values).  ``rows`` is an
+    int64 array of flat row ids (b*H + h)*Lq + i; None means every row.
+    Returns (out [n, Dv] float64, lse [n] float64).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    B, H, Lq, D = q.shape
+    Lkv, Dv = k.shape[2], v.shape[3]
+    assert k.shape == (B, H, Lkv, D) and v.shape == (B, H, Lkv, Dv)
+    if rows is None:
+        rows = np.arange(B * H * Lq, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    out = np.zeros((n, Dv), np.float64)
+    lse = np.zeros(n, np.float64)
+    score_kind = SCORE_KINDS[score.get("kind", "identity")]
+    bias_max = float(score.get("bias_max", 8.0))
+    lib = _load()
+    margs = _mask_args(mask)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    qp, kp, vp = (a.ctypes.data_as(f32p) for a in (q, k, v))
+
+    def run(lo, hi):
+        if hi <= lo:
+            return 0
+        return lib.oracle_attention_rows(
+            qp, kp, vp, B, H, Lq, Lkv, D, Dv, *margs, score_kind, bias_max,
+            float(scale),
+            rows[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), hi - lo,
+            out[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            lse[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        )
+
+    nthr = threads or _cpu_threads()
+    chunk = max(1, -(-n // (nthr * 4)))
+    bounds = [(s, min(n, s + chunk)) for s in range(0, n, chunk)]
+    if nthr == 1 or len(bounds) <= 1:
+        codes = [run(lo, hi) for lo, hi in bounds]
+    else:
+        with ThreadPoolExecutor(nthr) as ex:
+            codes = list(ex.map(lambda b: run(*b), bounds))
+    if any(c != 0 for c in codes):
+        raise ValueError("oracle_attention_rows rejected its arguments")
+    return out, lse
+
+
+def threads_used(threads: int | None = None) -> int:
+    return threads or _cpu_threads()
