@@ -1,0 +1,245 @@
+"""Throughput of the block-sparse masked attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = the whole hot path over one batch of seeded synthetic input that
+is already resident in HBM: build the block mask on the device, then run the
+forward.  Prints ONE JSON line.  `value` is effective TFLOP/s over unmasked
+FLOPs, 4 * B * H * D * (visible query-key pairs) per step, divided by the
+measured step time; `roofline` reports the forward kernel alone, timed with
+HIP events on the stream it is launched on; `cpu_baseline` times the fp64
+oracle on a bounded sample of rows of the same workload.
+
+`--copy-calibration` instead runs only a plain device-to-device copy of a
+known size, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be
+scaled against it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32-input instance)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_prefix_causal_traffic.txt")
+
+
+def visible_pairs(mask: dict, q_len: int, kv_len: int) -> int:
+    """Number of (query, key) pairs the mask leaves visible in one head."""
+    return int(_row_counts(mask, q_len, kv_len).sum())
+
+
+def kernel_source_hash() -> str:
+    """Hash of the sources the forward kernel is built from; the stored traffic
+    figures are only reported while it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_masked_flexattention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")) and (name.startswith("fwd_") or name == "internal.hpp"):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_name: str):
+    """HBM bytes per forward launch from the committed counter summary, or
+    None when it is missing, for another workload, or for other sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("workload") != workload_name or kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, q, k, v, target_seconds: float, seed: int = 0):
+    """Time the fp64 oracle on randomly sampled query rows of the workload,
+    growing the sample until it takes about `target_seconds`."""
+    from oracle import oracle
+
+    B, H, L, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["d"]
+    qf, kf, vf = (t.float().numpy() for t in (q, k, v))
+    rng = np.random.default_rng(seed)
+    threads = oracle.threads_used()
+    # per-row visible counts, to price the sample in unmasked FLOPs
+    counts = _row_counts(cfg["mask"], L, cfg["kv_len"])
+    n = max(threads, 16)
+    spent, flops, rows_done = 0.0, 0.0, 0
+    while True:
+        rows = rng.integers(0, B * H * L, size=n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention_rows(qf, kf, vf, cfg["mask"], cfg["score"], cfg["scale"], rows=rows,
+                              threads=threads)
+        dt = time.perf_counter() - t0
+        spent += dt
+        flops += 4.0 * D * float(counts[rows % L].sum())
+        rows_done += n
+        if spent >= target_seconds:
+            break
+        # aim the next batch at the remaining time
+        per_row = dt / n
+        n = int(min(max(n * 2, 16), max(16, (target_seconds - spent) / max(per_row, 1e-9))))
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d query rows drawn uniformly from all B*H*Lq rows of the workload, "
+                  "fp64 oracle, %.1f s" % (rows_done, spent),
+    }
+
+
+def _row_counts(mask, q_len, kv_len):
+    """Visible keys per query row, from each row's visible interval."""
+    i = np.arange(q_len, dtype=np.int64)
+    lo = np.zeros(q_len, np.int64)
+    hi = np.full(q_len, kv_len - 1, np.int64)
+    if mask["kind"] == "causal":
+        hi = np.minimum(hi, i)
+    elif mask["kind"] == "sliding_window":
+        lo = np.maximum(0, i - mask["window"])
+        hi = np.minimum(hi, i - mask.get("window_min", 0))
+    elif mask["kind"] == "prefix_causal":
+        P = mask["prefix"]
+        hi = np.minimum(hi, np.where(i <= P, np.maximum(P, i), i))
+    return np.maximum(hi - lo + 1, 0)
+
+
+def copy_calibration(nbytes: int, reps: int):
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    src.random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--use-subtiling", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from block_sparse_masked_flexattention_amd import flexattn as fa
+    from block_sparse_masked_flexattention_amd.inputs import BENCH_WORKLOAD, make_inputs, workload
+
+    if args.copy_calibration:
+        copy_calibration(1 << 30, 5)
+        return 0
+
+    name = args.workload or BENCH_WORKLOAD
+    cfg = workload(name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa.load()  # fails loudly if the HIP library is missing
+
+    q, k, v = make_inputs(cfg)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
+    out = torch.empty((B, H, Lq, D), dtype=qd.dtype, device=dev)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if cfg["lse"] else None
+    bm = fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], out=bm)
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out, lse=lse,
+               use_subtiling=args.use_subtiling)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in events]
+    fwd_avg_ms = float(np.mean(fwd_ms))
+    pairs = visible_pairs(cfg["mask"], Lq, Lk)
+    flops = 4.0 * B * H * D * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+    traffic = stored_traffic(name)
+
+    res = {
+        "metric": "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, flex-attn fwd",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
+            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"], "mask": cfg["mask"],
+            "score_mod": cfg["score"]["kind"], "out_dtype": cfg["dtype"], "lse": cfg["lse"],
+            "use_subtiling": args.use_subtiling, "visible_pairs_per_head": pairs,
+            "step": "block-mask build + forward",
+        },
+        "pct_peak": round(100.0 * value / peak, 2),
+        "fwd_ms": round(fwd_avg_ms, 5),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 5),
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

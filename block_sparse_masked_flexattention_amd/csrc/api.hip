@@ -1,0 +1,182 @@
+// api.hip -- the extern "C" entry points of libflexattn.so (declared in
+// include/flexattn.h).  Host-side validation, then one kernel launch on the
+// caller's stream.  Nothing here allocates, synchronises or keeps state.
+#include <math.h>
+
+#include "internal.hpp"
+
+using namespace flexattn;
+
+namespace {
+
+bool mask_ok(const flex_mask_desc& m, int32_t* err) {
+  switch (m.kind) {
+    case FLEX_MASK_NOOP:
+    case FLEX_MASK_CAUSAL:
+      return true;
+    case FLEX_MASK_SLIDING_WINDOW:
+      if (m.window_min < 0 || m.window < m.window_min) {
+        *err = FLEX_E_INVALID_ARG;
+        return false;
+      }
+      return true;
+    case FLEX_MASK_PREFIX_CAUSAL:
+      if (m.prefix < 0) {
+        *err = FLEX_E_INVALID_ARG;
+        return false;
+      }
+      return true;
+    default:
+      *err = FLEX_E_UNSUPPORTED;
+      return false;
+  }
+}
+
+int32_t ceil_div(int32_t a, int32_t b) { return (int32_t)(((int64_t)a + b - 1) / b); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t flex_attn_abi_version(void) { return FLEXATTN_ABI_VERSION; }
+
+const char* flex_attn_strerror(int32_t code) {
+  switch (code) {
+    case FLEX_OK:
+      return "success";
+    case FLEX_E_INVALID_ARG:
+      return "invalid argument";
+    case FLEX_E_UNSUPPORTED:
+      return "unsupported configuration (no kernel instance for it)";
+    case FLEX_E_HIP:
+      return "HIP launch error";
+    default:
+      return "unknown status code";
+  }
+}
+
+int32_t flex_attn_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t q_block,
+                                  int32_t kv_block, int32_t* n_q_blocks,
+                                  int32_t* n_kv_blocks) {
+  if (!n_q_blocks || !n_kv_blocks || q_len < 0 || kv_len < 0 || q_block <= 0 ||
+      kv_block <= 0)
+    return FLEX_E_INVALID_ARG;
+  *n_q_blocks = ceil_div(q_len, q_block);
+  *n_kv_blocks = ceil_div(kv_len, kv_block);
+  return FLEX_OK;
+}
+
+int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
+                                   int32_t kv_len, int32_t q_block,
+                                   int32_t kv_block, int32_t* kv_num_blocks,
+                                   int32_t* kv_indices,
+                                   int32_t* full_kv_num_blocks,
+                                   int32_t* full_kv_indices, void* stream) {
+  if (!mask) return FLEX_E_INVALID_ARG;
+  if (q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0 ||
+      q_block > 1024 || kv_block > 1024)
+    return FLEX_E_INVALID_ARG;
+  int32_t err = FLEX_OK;
+  if (!mask_ok(*mask, &err)) return err;
+  const int32_t nq = ceil_div(q_len, q_block), nk = ceil_div(kv_len, kv_block);
+  if ((int64_t)nq * nk > INT32_MAX) return FLEX_E_INVALID_ARG;
+  if (nq > 0 && (!kv_num_blocks || !full_kv_num_blocks)) return FLEX_E_INVALID_ARG;
+  if (nq > 0 && nk > 0 && (!kv_indices || !full_kv_indices)) return FLEX_E_INVALID_ARG;
+  if (nq == 0) return FLEX_OK;
+
+  MaskBuildParams p;
+  p.kind = mask->kind;
+  p.window = mask->window;
+  p.window_min = mask->window_min;
+  p.prefix = mask->prefix;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.q_block = q_block;
+  p.kv_block = kv_block;
+  p.n_qb = nq;
+  p.n_kb = nk;
+  p.kv_num = kv_num_blocks;
+  p.kv_idx = kv_indices;
+  p.fkv_num = full_kv_num_blocks;
+  p.fkv_idx = full_kv_indices;
+  return launch_block_mask(p, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FLEX_OK
+             : FLEX_E_HIP;
+}
+
+int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
+                      int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
+                      int32_t kv_len, int32_t head_dim,
+                      const flex_block_mask* bm, const flex_score_desc* score,
+                      float scale, void* out, int32_t out_dtype, float* lse,
+                      const flex_fwd_options* opt, void* stream) {
+  if (!bm) return FLEX_E_INVALID_ARG;
+  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0)
+    return FLEX_E_INVALID_ARG;
+  if (in_dtype != FLEX_DTYPE_BF16 && in_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
+  if (out_dtype != FLEX_DTYPE_BF16 && out_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
+  if (!isfinite(scale) || scale == 0.0f) return FLEX_E_UNSUPPORTED;
+  if (bm->q_len != q_len || bm->kv_len != kv_len) return FLEX_E_INVALID_ARG;
+  if (bm->q_block <= 0 || bm->kv_block <= 0) return FLEX_E_INVALID_ARG;
+  if (bm->n_q_blocks != ceil_div(q_len, bm->q_block) ||
+      bm->n_kv_blocks != ceil_div(kv_len, bm->kv_block))
+    return FLEX_E_INVALID_ARG;
+  int32_t err = FLEX_OK;
+  if (!mask_ok(bm->mask, &err)) return err;
+  int32_t score_kind = FLEX_SCORE_IDENTITY;
+  float bias_max = 0.f;
+  if (score) {
+    score_kind = score->kind;
+    if (score_kind != FLEX_SCORE_IDENTITY && score_kind != FLEX_SCORE_REL_BIAS)
+      return FLEX_E_UNSUPPORTED;
+    if (score_kind == FLEX_SCORE_REL_BIAS) {
+      if (score->num_heads != H || !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      bias_max = score->bias_max;
+    }
+  }
+  if (!fwd_supported(in_dtype, head_dim, bm->q_block, bm->kv_block))
+    return FLEX_E_UNSUPPORTED;
+
+  const int64_t rows = (int64_t)B * H * q_len;
+  const int64_t nwg = (int64_t)B * H * bm->n_q_blocks;
+  if (nwg > INT32_MAX || rows * head_dim > ((int64_t)1 << 40)) return FLEX_E_INVALID_ARG;
+  if (rows == 0) return FLEX_OK;  // nothing to write
+  if (!q || !out) return FLEX_E_INVALID_ARG;
+  if (kv_len > 0 && (!k || !v)) return FLEX_E_INVALID_ARG;
+  if (!bm->kv_num_blocks || !bm->full_kv_num_blocks) return FLEX_E_INVALID_ARG;
+  if (bm->n_kv_blocks > 0 && (!bm->kv_indices || !bm->full_kv_indices))
+    return FLEX_E_INVALID_ARG;
+  const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
+  if (align & 15u) return FLEX_E_INVALID_ARG;
+
+  FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.kv_num = bm->kv_num_blocks;
+  p.kv_idx = bm->kv_indices;
+  p.fkv_num = bm->full_kv_num_blocks;
+  p.fkv_idx = bm->full_kv_indices;
+  p.B = B;
+  p.H = H;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.n_qb = bm->n_q_blocks;
+  p.n_kb = bm->n_kv_blocks;
+  p.window = bm->mask.window;
+  p.window_min = bm->mask.window_min;
+  p.prefix = bm->mask.prefix;
+  p.c1 = fabsf(scale) * 1.44269504088896340736f;
+  p.neg_q = scale < 0.f ? 1 : 0;
+  p.bias_max = bias_max;
+  p.out_bf16 = out_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
+  const bool sub = opt != nullptr && opt->use_subtiling != 0;
+  return launch_fwd(p, in_dtype, head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
+                    score_kind, sub, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FLEX_OK
+             : FLEX_E_HIP;
+}
+
+}  // extern "C"

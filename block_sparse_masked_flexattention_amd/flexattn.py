@@ -1,0 +1,225 @@
+"""ctypes binding of libflexattn.so (the C ABI in include/flexattn.h).
+
+Argument marshalling only: every step of the attention forward and of the
+block-mask build runs in the library's HIP kernels.  PyTorch supplies device
+memory and the current HIP stream.  There is no fallback: if the library has
+not been built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflexattn.so")
+
+FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP = 0, 1, 2, 3
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3}
+SCORE_KINDS = {"identity": 0, "rel_bias": 1}
+ABI_VERSION = 1
+
+# the functions include/flexattn.h declares
+EXPORTED = (
+    "flex_attn_abi_version",
+    "flex_attn_strerror",
+    "flex_attn_block_mask_dims",
+    "flex_attn_build_block_mask",
+    "flex_attn_fwd",
+)
+
+
+class FlexAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, strerror(code), code))
+
+
+class MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("window_min", ctypes.c_int32), ("prefix", ctypes.c_int32)]
+
+
+class BlockMaskStruct(ctypes.Structure):
+    _fields_ = [("mask", MaskDesc),
+                ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+                ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
+                ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
+                ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
+                ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+
+
+class ScoreDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("bias_max", ctypes.c_float)]
+
+
+class FwdOptions(ctypes.Structure):
+    _fields_ = [("use_subtiling", ctypes.c_int32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str | None = None):
+    """Load the built library (raises if it is missing: build it with
+    ``python -m block_sparse_masked_flexattention_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise FileNotFoundError(
+                "libflexattn.so is not built (%s); run "
+                "`python -m block_sparse_masked_flexattention_amd.build`" % p)
+        lib = ctypes.CDLL(p)
+        i32, vp = ctypes.c_int32, ctypes.c_void_p
+        lib.flex_attn_abi_version.argtypes = []
+        lib.flex_attn_abi_version.restype = i32
+        lib.flex_attn_strerror.argtypes = [i32]
+        lib.flex_attn_strerror.restype = ctypes.c_char_p
+        lib.flex_attn_block_mask_dims.argtypes = [i32, i32, i32, i32,
+                                                  ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.flex_attn_block_mask_dims.restype = i32
+        lib.flex_attn_build_block_mask.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32, i32,
+                                                   vp, vp, vp, vp, vp]
+        lib.flex_attn_build_block_mask.restype = i32
+        lib.flex_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(BlockMaskStruct), ctypes.POINTER(ScoreDesc),
+                                      ctypes.c_float, vp, i32, vp,
+                                      ctypes.POINTER(FwdOptions), vp]
+        lib.flex_attn_fwd.restype = i32
+        if lib.flex_attn_abi_version() != ABI_VERSION:
+            raise RuntimeError("libflexattn.so ABI version mismatch")
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    return load().flex_attn_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != FLEX_OK:
+        raise FlexAttnError(code, where)
+
+
+def default_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) as float32 -- 0.125 at head_dim 64, 0.5 at 4."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+
+
+def mask_desc(mask: dict) -> MaskDesc:
+    return MaskDesc(MASK_KINDS[mask["kind"]], int(mask.get("window", 0)),
+                    int(mask.get("window_min", 0)), int(mask.get("prefix", 0)))
+
+
+def block_mask_dims(q_len: int, kv_len: int, q_block: int, kv_block: int):
+    nq, nk = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().flex_attn_block_mask_dims(q_len, kv_len, q_block, kv_block,
+                                            ctypes.byref(nq), ctypes.byref(nk)),
+           "flex_attn_block_mask_dims")
+    return nq.value, nk.value
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class BlockMask:
+    """The kv half of a FlexAttention block mask, on the device."""
+    mask: dict
+    q_len: int
+    kv_len: int
+    q_block: int
+    kv_block: int
+    kv_num_blocks: torch.Tensor       # int32 [nQB]
+    kv_indices: torch.Tensor          # int32 [nQB, nKVB]
+    full_kv_num_blocks: torch.Tensor  # int32 [nQB]
+    full_kv_indices: torch.Tensor     # int32 [nQB, nKVB]
+
+    def as_struct(self) -> BlockMaskStruct:
+        nq, nk = self.kv_indices.shape
+        return BlockMaskStruct(
+            mask_desc(self.mask), self.q_len, self.kv_len, self.q_block, self.kv_block,
+            nq, nk, self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
+            self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr())
+
+    def arrays(self):
+        return (self.kv_num_blocks, self.kv_indices, self.full_kv_num_blocks,
+                self.full_kv_indices)
+
+
+def build_block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int,
+                     device="cuda", out: BlockMask | None = None) -> BlockMask:
+    """Build the block arrays for a mask kind on the device (asynchronously,
+    on the current stream).  ``out`` reuses existing arrays of the right size."""
+    nq, nk = block_mask_dims(q_len, kv_len, q_block, kv_block)
+    if out is None:
+        dev = torch.device(device)
+        z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
+        out = BlockMask(dict(mask), q_len, kv_len, q_block, kv_block,
+                        z(nq), z(nq, nk), z(nq), z(nq, nk))
+    arrs = out.arrays()
+    for a, shape in zip(arrs, [(nq,), (nq, nk), (nq,), (nq, nk)]):
+        if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
+            raise ValueError("block-mask arrays have the wrong dtype/shape")
+    md = mask_desc(mask)
+    dev = arrs[0].device
+    _check(load().flex_attn_build_block_mask(
+        ctypes.byref(md), q_len, kv_len, q_block, kv_block,
+        *[a.data_ptr() for a in arrs], _stream_handle(dev)), "flex_attn_build_block_mask")
+    return out
+
+
+_DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
+        score: dict | None = None, scale: float | None = None, *,
+        out_dtype: torch.dtype | None = None, return_lse: bool = False,
+        use_subtiling: bool = False, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """Masked block-sparse attention forward.  q [B,H,Lq,D], k/v [B,H,Lkv,D]
+    (bfloat16 or float32, contiguous, on the GPU).  Returns (out, lse) with lse
+    None unless requested."""
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+        raise ValueError("q/k/v shapes disagree")
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q/k/v must share a dtype in {bfloat16, float32}")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q/k/v must be contiguous GPU tensors")
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, Lq, D), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, H, Lq, D) or out.dtype not in _DT or not out.is_contiguous():
+        raise ValueError("bad out tensor")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
+                            or not lse.is_contiguous()):
+        raise ValueError("bad lse tensor")
+    sc = score or {"kind": "identity"}
+    sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
+                   float(sc.get("bias_max", 8.0)))
+    opt = FwdOptions(1 if use_subtiling else 0)
+    bm = block_mask.as_struct()
+    scale = default_scale(D) if scale is None else float(scale)
+    _check(load().flex_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], B, H, Lq, Lk, D,
+        ctypes.byref(bm), ctypes.byref(sd), scale, out.data_ptr(), _DT[out.dtype],
+        lse.data_ptr() if lse is not None else None, ctypes.byref(opt),
+        _stream_handle(q.device)), "flex_attn_fwd")
+    return out, (lse if return_lse or lse is not None else None)

@@ -1,0 +1,179 @@
+/*
+ * flexattn.h -- C ABI of the MI355X (gfx950) block-sparse masked attention
+ * forward library, libflexattn.so.
+ *
+ * The operation is the FlexAttention forward pass: a block mask lists, per
+ * Q_BLOCK-row block of queries, which KV_BLOCK-wide key blocks are partially
+ * visible (kv_num_blocks / kv_indices) and which are fully visible
+ * (full_kv_num_blocks / full_kv_indices); the forward walks those lists,
+ * forms S = scale * Q K^T tile by tile, applies the score modification on
+ * every visited tile and the mask only on partial tiles, runs the online
+ * softmax (running row max, alpha rescale of the accumulator and row sum)
+ * and accumulates P V, optionally writing the log-sum-exp.
+ *   - Block-mask tuple fields: "[Inductor][Flex Attention] Add Subtiling
+ *     Option for Alpha Scaling", test/inductor/test_flex_attention.py hunk
+ *     (the tuple passed to the flex_attention higher-order op).
+ *   - Online-softmax step and the alpha-rescale subtiling option: same page,
+ *     common.py.jinja hunk in forward_block_mn, and the USE_SUBTILING entry
+ *     of FlexKernelOptions in torch/nn/attention/flex_attention.py.
+ *   - Mask semantics (prefix-bidirectional OR causal, inclusive bound,
+ *     masked score = -inf): "Performance for templated attention strangely
+ *     bad for a combination of causal + upper square mask", bad.py -> bad2.py.
+ *
+ * Conventions for every entry point:
+ *   - Returns FLEX_OK (0) or a FLEX_E_* code; never throws, never aborts.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates or frees device memory, never synchronises the
+ *     stream, keeps no pointer after it returns and holds no state between
+ *     calls.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream); results are ready when that stream reaches them.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     on such an error nothing is launched and no output is touched.
+ *   - FLEX_E_HIP means a HIP launch reported an error (hipGetLastError);
+ *     outputs are then undefined.
+ *   - Calls are thread-safe (no shared mutable state).
+ */
+#ifndef FLEXATTN_H
+#define FLEXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLEXATTN_ABI_VERSION 1
+
+/* ---- status codes ---- */
+#define FLEX_OK 0
+#define FLEX_E_INVALID_ARG 1 /* null pointer, negative or mismatched size */
+#define FLEX_E_UNSUPPORTED 2 /* valid but not built: head dim, block size, dtype */
+#define FLEX_E_HIP 3         /* a HIP launch failed */
+
+/* ---- element types ---- */
+#define FLEX_DTYPE_BF16 0
+#define FLEX_DTYPE_FP32 1
+
+/* ---- mask kinds (mask_mod) ----
+ * For query index i and key index j (0-based, i < q_len, j < kv_len):
+ *   NOOP            every key is visible
+ *   CAUSAL          i >= j
+ *   SLIDING_WINDOW  window_min <= i - j <= window   (window_min = 0: the
+ *                   causal sliding window of width window + 1)
+ *   PREFIX_CAUSAL   (i <= prefix AND j <= prefix) OR i >= j   (inclusive
+ *                   bound, as in the bad.py mask of the templated-attention
+ *                   performance issue) */
+#define FLEX_MASK_NOOP 0
+#define FLEX_MASK_CAUSAL 1
+#define FLEX_MASK_SLIDING_WINDOW 2
+#define FLEX_MASK_PREFIX_CAUSAL 3
+
+typedef struct flex_mask_desc {
+  int32_t kind;       /* FLEX_MASK_* */
+  int32_t window;     /* SLIDING_WINDOW: largest visible i - j (>= window_min) */
+  int32_t window_min; /* SLIDING_WINDOW: smallest visible i - j (>= 0) */
+  int32_t prefix;     /* PREFIX_CAUSAL: last index of the bidirectional prefix (>= 0) */
+} flex_mask_desc;
+
+/* ---- score modifications (score_mod), applied to the SCALED score s ----
+ *   IDENTITY  s
+ *   REL_BIAS  s - slope_h * (i - j),  slope_h = 2^(-bias_max * (h + 1) / H),
+ *             h the head index, H = num_heads (an ALiBi-style bias). */
+#define FLEX_SCORE_IDENTITY 0
+#define FLEX_SCORE_REL_BIAS 1
+
+typedef struct flex_score_desc {
+  int32_t kind;      /* FLEX_SCORE_* */
+  int32_t num_heads; /* REL_BIAS: H in the slope formula; must equal the call's H */
+  float bias_max;    /* REL_BIAS: 8 for the usual ALiBi slopes; finite */
+} flex_score_desc;
+
+/* ---- block mask, as consumed by flex_attn_fwd ----
+ * Built by flex_attn_build_block_mask (or by the caller, in the same format):
+ *   kv_num_blocks[qb]            number of partial tiles of q-block qb
+ *   kv_indices[qb * n_kv_blocks + n], n < kv_num_blocks[qb]: their kv-block
+ *                                indices (the rest of the row is padding)
+ *   full_kv_num_blocks / full_kv_indices: the same for full tiles.
+ * A tile is full when every (i, j) in it is visible and in range, partial
+ * when some are, and listed in neither array when none are.  The mask
+ * descriptor travels with the arrays because partial tiles evaluate it per
+ * element.  The forward reads the arrays on the device; entries outside
+ * [0, n_kv_blocks) are clamped, so a malformed array gives wrong results but
+ * no out-of-bounds access. */
+typedef struct flex_block_mask {
+  flex_mask_desc mask;
+  int32_t q_len, kv_len;           /* sequence lengths the mask was built for */
+  int32_t q_block, kv_block;       /* Q_BLOCK, KV_BLOCK */
+  int32_t n_q_blocks, n_kv_blocks; /* ceil(q_len / q_block), ceil(kv_len / kv_block) */
+  const int32_t* kv_num_blocks;      /* device, [n_q_blocks] */
+  const int32_t* kv_indices;         /* device, [n_q_blocks, n_kv_blocks] */
+  const int32_t* full_kv_num_blocks; /* device, [n_q_blocks] */
+  const int32_t* full_kv_indices;    /* device, [n_q_blocks, n_kv_blocks] */
+} flex_block_mask;
+
+typedef struct flex_fwd_options {
+  /* USE_SUBTILING: rescale the output accumulator by alpha in two halves of
+   * the head dimension, each just before the P V products that update it.
+   * Results are bitwise identical either way; only instruction order changes. */
+  int32_t use_subtiling;
+} flex_fwd_options;
+
+/* Returns FLEXATTN_ABI_VERSION. */
+int32_t flex_attn_abi_version(void);
+
+/* Human-readable text for a status code; a static string, never NULL. */
+const char* flex_attn_strerror(int32_t code);
+
+/* Host only.  n_q_blocks = ceil(q_len / q_block), n_kv_blocks =
+ * ceil(kv_len / kv_block).  Lengths may be 0; block sizes must be > 0.
+ * Errors: FLEX_E_INVALID_ARG (null output pointer, negative length,
+ * non-positive block size). */
+int32_t flex_attn_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t q_block,
+                                  int32_t kv_block, int32_t* n_q_blocks,
+                                  int32_t* n_kv_blocks);
+
+/* Build the four block arrays for a mask kind on the device.
+ *   mask        host pointer to the mask descriptor.
+ *   q_len, kv_len >= 0 (any value: the last blocks may be ragged).
+ *   q_block, kv_block: 1 .. 1024.
+ *   outputs: device int32 arrays, [n_q_blocks] and [n_q_blocks * n_kv_blocks].
+ *   Every index row is written in full: the selected kv-blocks in ascending
+ *   order, then every other kv-block in ascending order.
+ * Errors: FLEX_E_INVALID_ARG (null pointer with a non-empty output, bad sizes,
+ * bad mask parameters), FLEX_E_UNSUPPORTED (unknown mask kind), FLEX_E_HIP. */
+int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
+                                   int32_t kv_len, int32_t q_block,
+                                   int32_t kv_block, int32_t* kv_num_blocks,
+                                   int32_t* kv_indices,
+                                   int32_t* full_kv_num_blocks,
+                                   int32_t* full_kv_indices, void* stream);
+
+/* Attention forward.
+ *   q [B, H, q_len, head_dim], k [B, H, kv_len, head_dim],
+ *   v [B, H, kv_len, head_dim]: contiguous, element type in_dtype, 16-byte
+ *   aligned device pointers.
+ *   bm: host pointer; bm->q_len / kv_len must equal the call's; its block
+ *   sizes select the kernel.  bm->mask is applied on partial tiles.
+ *   score: host pointer, NULL = identity.
+ *   scale: finite and non-zero (pass 1/sqrt(head_dim) for the usual default).
+ *   out [B, H, q_len, head_dim] of out_dtype, contiguous, 16-byte aligned.
+ *   lse: NULL, or fp32 [B, H, q_len]: natural-log log-sum-exp of the scores
+ *   of each row; -inf (and out = 0) for a row that sees no key.
+ *   opt: host pointer, NULL = defaults (no subtiling).
+ * Built instances: in_dtype BF16 or FP32; head_dim 64 or 128;
+ * (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}; any mask kind and
+ * score kind; out_dtype BF16 or FP32.  q_len, kv_len >= 0 (ragged last
+ * blocks are fine), B, H >= 0, B * H * n_q_blocks < 2^31.
+ * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP. */
+int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
+                      int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
+                      int32_t kv_len, int32_t head_dim,
+                      const flex_block_mask* bm, const flex_score_desc* score,
+                      float scale, void* out, int32_t out_dtype, float* lse,
+                      const flex_fwd_options* opt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXATTN_H */

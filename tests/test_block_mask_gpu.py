@@ -1,0 +1,67 @@
+"""GPU block-mask builder vs the oracle's brute-force enumeration: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_masked_flexattention_amd import flexattn as fa
+from block_sparse_masked_flexattention_amd.inputs import WORKLOADS, workload
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_arrays(mask, q_len, kv_len, qb, kb):
+    bm = fa.build_block_mask(mask, q_len, kv_len, qb, kb, device="cuda:0")
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in bm.arrays()]
+
+
+def _assert_same(mask, q_len, kv_len, qb, kb):
+    got = _gpu_arrays(mask, q_len, kv_len, qb, kb)
+    ref = oracle.block_mask(mask, q_len, kv_len, qb, kb)
+    for name, g, r in zip(["kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                           "full_kv_indices"], got, ref):
+        assert g.dtype == np.int32
+        np.testing.assert_array_equal(g, r, err_msg="%s %s %s" % (name, mask, (q_len, kv_len, qb, kb)))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_block_masks(name):
+    cfg = workload(name)
+    _assert_same(cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        kind = ["noop", "causal", "sliding_window", "prefix_causal"][rng.integers(4)]
+        q_len, kv_len = int(rng.integers(0, 301)), int(rng.integers(0, 301))
+        qb, kb = int(rng.choice([16, 32, 64, 128])), int(rng.choice([16, 32, 64, 128]))
+        mask = {"kind": kind}
+        if kind == "sliding_window":
+            wmin = int(rng.integers(0, 20))
+            mask.update(window_min=wmin, window=wmin + int(rng.integers(0, 120)))
+        if kind == "prefix_causal":
+            mask["prefix"] = int(rng.integers(0, 300))
+        cases.append((mask, q_len, kv_len, qb, kb))
+    return cases
+
+
+def test_random_tiny_shapes():
+    for case in _random_cases(80, seed=7):
+        _assert_same(*case)
+
+
+@pytest.mark.parametrize("case", [
+    ({"kind": "causal"}, 0, 0, 64, 64),
+    ({"kind": "causal"}, 5, 0, 64, 64),
+    ({"kind": "causal"}, 1, 1, 1, 1),
+    ({"kind": "noop"}, 1000, 1000, 1024, 1024),
+    ({"kind": "causal"}, 700, 1300, 1, 128),
+    ({"kind": "sliding_window", "window": 2000000000, "window_min": 0}, 300, 300, 32, 32),
+    ({"kind": "prefix_causal", "prefix": 0}, 200, 200, 64, 32),
+    ({"kind": "noop"}, 20, 700, 16, 2),  # more kv-blocks than threads per work-group
+])
+def test_edge_shapes(case):
+    _assert_same(*case)

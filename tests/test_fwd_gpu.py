@@ -1,0 +1,216 @@
+"""GPU forward vs the fp64 oracle, through the C ABI.
+
+Tolerances (see tests/parity.py): bf16 inputs -> out max-abs 1e-2 (fp32 out;
+bf16 out adds half a bf16 ulp of the reference), lse 1e-3; fp32 inputs ->
+1e-4; rows that see no key -> exactly 0 and -inf.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_masked_flexattention_amd import flexattn as fa
+from block_sparse_masked_flexattention_amd.inputs import make_inputs, workload
+from parity import compare, oracle_rows, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_compare(cfg, out_dtype, use_subtiling=False, scale=None):
+    q, k, v = make_inputs(cfg)
+    in_dt = cfg["dtype"]
+    od = {"bf16": torch.bfloat16, "fp32": torch.float32}[out_dtype]
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=od, lse=True, use_subtiling=use_subtiling,
+                          scale=scale)
+    ref_out, ref_lse = oracle_rows(cfg, q, k, v, scale=scale)
+    D = cfg["d"]
+    return compare(out.reshape(-1, D), lse.reshape(-1), ref_out, ref_lse, in_dt, out_dtype,
+                   what=cfg["name"])
+
+
+# Reduced versions of each workload: several tiles in both directions and a
+# ragged tail in both lengths.
+SMALL = [
+    ("tiny_causal", {}),
+    ("tiny_causal", dict(q_len=200, kv_len=200)),
+    ("tiny_causal", dict(q_block=128, kv_block=128, q_len=300, kv_len=300, d=128)),
+    ("prefix_causal", dict(B=1, H=2, q_len=1000, kv_len=1000, mask={"kind": "prefix_causal", "prefix": 300})),
+    ("prefix_causal", dict(B=2, H=1, q_len=520, kv_len=520, mask={"kind": "prefix_causal", "prefix": 256})),
+    ("sliding_window", dict(B=1, H=2, q_len=1100, kv_len=1100)),
+    ("sliding_window", dict(B=1, H=1, q_len=700, kv_len=700, mask={"kind": "sliding_window", "window": 100, "window_min": 3})),
+    ("long_causal_d128", dict(B=1, H=2, q_len=777, kv_len=777)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=300, kv_len=300, q_block=64, kv_block=64)),
+    ("causal_rel_bias", dict(B=1, H=8, q_len=700, kv_len=700)),
+    ("causal_rel_bias", dict(B=1, H=3, q_len=333, kv_len=333, q_block=128, kv_block=64)),
+    ("prefix_causal", dict(B=1, H=2, q_len=300, kv_len=650, mask={"kind": "noop"})),
+    ("prefix_causal", dict(B=1, H=1, q_len=650, kv_len=300, mask={"kind": "causal"}, q_block=64, kv_block=64)),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_small_parity(name, over, out_dtype):
+    cfg = workload(name, **over)
+    if "d" in over:
+        cfg["scale"] = fa.default_scale(cfg["d"])
+    _full_compare(cfg, out_dtype)
+
+
+def test_small_parity_subtiling():
+    cfg = workload("sliding_window", B=1, H=2, q_len=1100, kv_len=1100)
+    _full_compare(cfg, "fp32", use_subtiling=True)
+
+
+def test_negative_scale():
+    cfg = workload("prefix_causal", B=1, H=1, q_len=300, kv_len=300)
+    _full_compare(cfg, "fp32", scale=-0.2)
+
+
+def test_fp32_rel_bias_and_window():
+    cfg = workload("tiny_causal", H=4, mask={"kind": "sliding_window", "window": 50},
+                   score={"kind": "rel_bias", "bias_max": 8.0})
+    _full_compare(cfg, "fp32")
+
+
+# ---- full-size workloads in the benchmark's launch configuration ----
+
+
+@pytest.mark.parametrize("name", ["prefix_causal", "sliding_window", "long_causal_d128",
+                                  "causal_rel_bias"])
+def test_full_size_sampled_rows(name):
+    cfg = workload(name)
+    q, k, v = make_inputs(cfg)
+    rows = sample_rows(cfg)
+    D = cfg["d"]
+    ref_out, ref_lse = oracle_rows(cfg, q, k, v, rows=rows)
+    for out_dtype in ("bf16", "fp32"):
+        od = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+        out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=od, lse=True)
+        compare(out.reshape(-1, D)[rows], lse.reshape(-1)[rows], ref_out, ref_lse, "bf16",
+                out_dtype, what=name + "/" + out_dtype)
+
+
+def test_full_size_tiny_causal():
+    _full_compare(workload("tiny_causal"), "fp32")
+
+
+# ---- invariants that hold bit for bit ----
+
+
+def _bitwise(a, b):
+    return np.array_equal(a.view(np.uint64), b.view(np.uint64)) if a.dtype == np.float64 else np.array_equal(a, b)
+
+
+def test_subtiling_is_bitwise_identical():
+    cfg = workload("sliding_window")
+    q, k, v = make_inputs(cfg)
+    o0, l0, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True, use_subtiling=False)
+    o1, l1, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True, use_subtiling=True)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_reruns_are_deterministic():
+    cfg = workload("prefix_causal", B=2, H=4)
+    q, k, v = make_inputs(cfg)
+    o0, _, _ = run_gpu(cfg, q, k, v)
+    o1, _, _ = run_gpu(cfg, q, k, v)
+    assert np.array_equal(o0, o1)
+
+
+def _demoted(bm, with_empty):
+    """Same visiting order, but every full tile listed as partial (and, with
+    with_empty, every empty tile appended to the partial list too)."""
+    kvn, kvi, fkn, fki = (a.cpu() for a in bm.arrays())
+    nq, nk = kvi.shape
+    n_kvi = torch.zeros_like(kvi)
+    n_kvn = torch.zeros_like(kvn)
+    for qb in range(nq):
+        lst = list(kvi[qb, :kvn[qb]]) + list(fki[qb, :fkn[qb]])
+        if with_empty:
+            lst += [kb for kb in range(nk) if kb not in set(int(x) for x in lst)]
+        lst = [int(x) for x in lst]
+        rest = [kb for kb in range(nk) if kb not in set(lst)]
+        n_kvi[qb] = torch.tensor(lst + rest, dtype=torch.int32)
+        n_kvn[qb] = len(lst)
+    dev = bm.kv_indices.device
+    return fa.BlockMask(bm.mask, bm.q_len, bm.kv_len, bm.q_block, bm.kv_block,
+                        n_kvn.to(dev), n_kvi.to(dev), torch.zeros_like(bm.full_kv_num_blocks),
+                        bm.full_kv_indices.clone())
+
+
+@pytest.mark.parametrize("name,over", [
+    ("prefix_causal", dict(B=1, H=2, q_len=1024, kv_len=1024, mask={"kind": "prefix_causal", "prefix": 300})),
+    ("causal_rel_bias", dict(B=1, H=8, q_len=512, kv_len=512)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=512, kv_len=512)),
+])
+def test_full_tiles_demoted_to_partial_are_bitwise_equal(name, over):
+    cfg = workload(name, **over)
+    q, k, v = make_inputs(cfg)
+    o0, l0, bm = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    for with_empty in (False, True):
+        o1, l1, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True,
+                            bm=_demoted(bm, with_empty))
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), with_empty
+
+
+def test_causal_row0_returns_v0_exactly():
+    cfg = workload("prefix_causal", B=1, H=2, q_len=256, kv_len=256, mask={"kind": "causal"})
+    q, k, v = make_inputs(cfg)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    np.testing.assert_array_equal(out[:, :, 0, :], v[:, :, 0, :].double().numpy())
+    s00 = (q[:, :, 0, :].double() * k[:, :, 0, :].double()).sum(-1) * cfg["scale"]
+    np.testing.assert_allclose(lse[:, :, 0], s00.numpy(), atol=1e-5)
+
+
+def test_uniform_scores_closed_form():
+    """q = 0: every visible key weighs the same, lse = ln(count)."""
+    cfg = workload("sliding_window", B=1, H=1, q_len=600, kv_len=600,
+                   mask={"kind": "sliding_window", "window": 130})
+    q, k, v = make_inputs(cfg)
+    q = torch.zeros_like(q)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    i = np.arange(600)
+    count = np.minimum(i, 130) + 1
+    np.testing.assert_allclose(lse[0, 0], np.log(count), atol=1e-5)
+    vv = v[0, 0].double().numpy()
+    csum = np.concatenate([np.zeros((1, vv.shape[1])), np.cumsum(vv, 0)])
+    mean = (csum[i + 1] - csum[i + 1 - count]) / count[:, None]
+    np.testing.assert_allclose(out[0, 0], mean, atol=1e-5)
+
+
+# ---- degenerate shapes ----
+
+
+def test_fully_masked_rows_and_blocks():
+    # window_min = 200 > 0: rows 0..199 see nothing; with 128-row q-blocks the
+    # first q-block has no tile at all
+    cfg = workload("sliding_window", B=1, H=2, q_len=520, kv_len=520,
+                   mask={"kind": "sliding_window", "window": 300, "window_min": 200})
+    max_out, _ = _full_compare(cfg, "fp32")
+    q, k, v = make_inputs(cfg)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    assert np.all(np.isneginf(lse[:, :, :200])) and np.all(out[:, :, :200] == 0)
+
+
+def test_no_keys():
+    cfg = workload("prefix_causal", B=1, H=2, q_len=130, kv_len=0)
+    q, k, v = make_inputs(cfg)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_no_queries_and_no_batch():
+    for over in (dict(q_len=0), dict(B=0)):
+        cfg = workload("prefix_causal", H=2, kv_len=256, **({"q_len": 256} | over))
+        q, k, v = make_inputs(cfg)
+        out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+        assert out.size == 0 and lse.size == 0
+
+
+def test_single_row_single_key():
+    cfg = workload("tiny_causal", q_len=1, kv_len=1)
+    q, k, v = make_inputs(cfg)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    np.testing.assert_array_equal(out[0, 0, 0], v[0, 0, 0].double().numpy())
+    assert math.isfinite(float(lse[0, 0, 0]))
