@@ -24,9 +24,13 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# amdgpu-mfma-vgpr-form: keep matrix-instruction accumulators in ordinary
+# VGPRs; the softmax reads every score and rescales the output accumulator,
+# and accumulators parked in AGPRs would cost a copy each way.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
@@ -36,8 +40,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *HIP_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
@@ -50,17 +54,22 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(jobs: int | None = None, extra=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(jobs: int | None = None, extra=(), out: str | None = None,
+          build_dir: str | None = None) -> str:
+    """Compile every .hip source and link the library.  `extra` adds hipcc
+    flags; `out` / `build_dir` place a variant build elsewhere."""
+    out = out or LIB_PATH
+    build_dir = build_dir or BUILD_DIR
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, len(os.sched_getaffinity(0))))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None):

@@ -9,13 +9,21 @@
 // of keys [lo_i, hi_i] (possibly empty).  A tile is classified from those row
 // intervals instead of from its q_block * kv_block elements:
 //   full    every row of the tile is in range and its interval covers all of
-//           the tile's columns (which must be in range too);
-//   partial some row's interval meets the tile's in-range columns;
+//           the tile's columns (which must be in range too): with
+//           LO = max_i lo_i and HI = min_i hi_i over the tile's rows, that is
+//           LO <= first column and HI >= last column;
+//   partial some row's interval meets the tile's columns, i.e. the tile lies
+//           in the union over rows of the kv-block ranges
+//           [lo_i / kv_block, hi_i / kv_block];
 //   empty   otherwise.
-// One work-group handles one q-block row of tiles: its threads classify the
-// kv-blocks, then a block-wide prefix count over the 0/1 classes gives each
-// kv-block its slot.  Rows are written in full: selected kv-blocks in
-// ascending order, then the others in ascending order.
+// One work-group handles one q-block row of tiles.  Its threads take the
+// rows (a block-wide max / min gives LO and HI; each row ORs its kv-block
+// range into an LDS bitmask, 256 kv-blocks at a time) and then the kv-blocks
+// (one per thread per chunk).  A block-wide prefix count over the 0/1 classes
+// gives each kv-block its slot: selected kv-blocks in ascending order, then
+// the others in ascending order.
+#include <climits>
+
 #include "internal.hpp"
 
 namespace flexattn {
@@ -23,9 +31,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = kThreads;  // kv-blocks classified per pass
 
 struct RowInterval {
-  int lo, hi;  // inclusive; empty when lo > hi
+  int lo, hi;  // inclusive, clipped to [0, kv_len - 1]; empty when lo > hi
 };
 
 __device__ inline RowInterval visible_keys(const MaskBuildParams& p, int i) {
@@ -37,10 +46,9 @@ __device__ inline RowInterval visible_keys(const MaskBuildParams& p, int i) {
       hi = min(hi, i);
       break;
     case FLEX_MASK_SLIDING_WINDOW: {
-      // window_min <= i - j <= window; computed in 64 bits so that
-      // i - window cannot overflow
-      long long l = (long long)i - p.window;
-      long long h = (long long)i - p.window_min;
+      // window_min <= i - j <= window, in 64 bits so i - window cannot wrap
+      const long long l = (long long)i - p.window;
+      const long long h = (long long)i - p.window_min;
       lo = (int)max(0LL, l);
       hi = (int)min((long long)hi, h);
       break;
@@ -52,37 +60,35 @@ __device__ inline RowInterval visible_keys(const MaskBuildParams& p, int i) {
   return {lo, hi};
 }
 
-// 0 empty, 1 partial, 2 full
-__device__ inline int classify(const MaskBuildParams& p, int qb, int kb) {
-  const int r0 = qb * p.q_block;
-  const int r1 = min(r0 + p.q_block, p.q_len);  // exclusive
-  const int c0 = kb * p.kv_block;
-  const int c_end = c0 + p.kv_block - 1;         // last column of the tile
-  const int c1 = min(c_end, p.kv_len - 1);       // last in-range column
-  bool any = false;
-  bool full = (r0 + p.q_block <= p.q_len) && (c_end < p.kv_len);
-  for (int i = r0; i < r1; ++i) {
-    RowInterval iv = visible_keys(p, i);
-    const bool nonempty = iv.lo <= iv.hi;
-    any |= nonempty && iv.lo <= c1 && iv.hi >= c0;
-    full &= nonempty && iv.lo <= c0 && iv.hi >= c_end;
-  }
-  return full ? 2 : (any ? 1 : 0);
+// Block-wide reductions through wave shuffles and a small LDS array.
+__device__ inline int block_max(int v, int* scratch) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = max(r, scratch[w]);
+  return r;
+}
+
+__device__ inline int block_min(int v, int* scratch) {
+  return -block_max(-v, scratch);
 }
 
 // Exclusive prefix count of a 0/1 flag over the work-group, plus the total.
-// Uses wave ballots; `wave_tot` is LDS scratch of kWaves ints.
-__device__ inline int block_prefix(bool flag, int* wave_tot, int* total) {
+__device__ inline int block_prefix(bool flag, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long bal = __ballot(flag);
   const int below = __popcll(bal & ((1ULL << lane) - 1ULL));
   __syncthreads();
-  if (lane == 0) wave_tot[wave] = __popcll(bal);
+  if (lane == 0) scratch[wave] = __popcll(bal);
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const int c = wave_tot[w];
+    const int c = scratch[w];
     before += w < wave ? c : 0;
     tot += c;
   }
@@ -90,44 +96,80 @@ __device__ inline int block_prefix(bool flag, int* wave_tot, int* total) {
   return before + below;
 }
 
+// Classes of kv-blocks [k0, k0 + kChunk) of this q-block row: bit t of
+// `touched` is set when some row's visible interval meets kv-block k0 + t.
+__device__ inline void mark_touched(const MaskBuildParams& p, int r0, int r1, int k0,
+                                    unsigned* touched) {
+  if (threadIdx.x < kChunk / 32) touched[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int i = r0 + (int)threadIdx.x; i < r1; i += kThreads) {
+    const RowInterval iv = visible_keys(p, i);
+    if (iv.lo > iv.hi) continue;
+    const int first = max(iv.lo / p.kv_block, k0) - k0;
+    const int last = min(iv.hi / p.kv_block, k0 + kChunk - 1) - k0;
+    for (int w = first >> 5; w <= (last >> 5) && first <= last; ++w) {
+      const int b0 = max(first, w * 32) - w * 32;
+      const int b1 = min(last, w * 32 + 31) - w * 32;
+      const unsigned bits = (b1 - b0 == 31) ? 0xffffffffu : (((1u << (b1 - b0 + 1)) - 1u) << b0);
+      atomicOr(&touched[w], bits);
+    }
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildParams p) {
-  __shared__ int wave_tot[kWaves];
+  __shared__ int scratch[kWaves];
+  __shared__ unsigned touched[kChunk / 32];
   const int qb = blockIdx.x;
   const int nk = p.n_kb;
-  const int row = qb * nk;
+  const size_t row = (size_t)qb * nk;
+  const int r0 = qb * p.q_block;
+  const int r1 = min(r0 + p.q_block, p.q_len);  // exclusive; r0 < r1 since qb < n_qb
 
-  // pass 1: totals of partial and full tiles in this q-block row
+  // LO = max lo_i, HI = min hi_i over the q-block's rows
+  int lo_max = INT_MIN, hi_min = INT_MAX;
+  for (int i = r0 + (int)threadIdx.x; i < r1; i += kThreads) {
+    const RowInterval iv = visible_keys(p, i);
+    lo_max = max(lo_max, iv.lo);
+    hi_min = min(hi_min, iv.hi);
+  }
+  lo_max = block_max(lo_max, scratch);
+  hi_min = block_min(hi_min, scratch);
+  const bool rows_in_range = r0 + p.q_block <= p.q_len;
+
+  // pass 0 counts, pass 1 writes
   int n_part = 0, n_full = 0;
-  for (int base = 0; base < nk; base += kThreads) {
-    const int kb = base + threadIdx.x;
-    const int c = kb < nk ? classify(p, qb, kb) : 0;
-    int tp, tf;
-    block_prefix(c == 1, wave_tot, &tp);
-    block_prefix(c == 2, wave_tot, &tf);
-    n_part += tp;
-    n_full += tf;
+  for (int pass = 0; pass < 2; ++pass) {
+    int seen_part = 0, seen_full = 0;
+    for (int k0 = 0; k0 < nk; k0 += kChunk) {
+      mark_touched(p, r0, r1, k0, touched);
+      const int kb = k0 + (int)threadIdx.x;
+      int c = 0;  // 0 empty, 1 partial, 2 full
+      if (kb < nk) {
+        const int c0 = kb * p.kv_block;
+        const int c_end = c0 + p.kv_block - 1;
+        const bool full = rows_in_range && c_end < p.kv_len && lo_max <= c0 && hi_min >= c_end;
+        const bool any = (touched[threadIdx.x >> 5] >> (threadIdx.x & 31)) & 1u;
+        c = full ? 2 : (any ? 1 : 0);
+      }
+      int tp, tf;
+      const int bp = seen_part + block_prefix(c == 1, scratch, &tp);
+      const int bf = seen_full + block_prefix(c == 2, scratch, &tf);
+      if (pass == 1 && kb < nk) {
+        // selected: after the selected ones before it; otherwise after all
+        // selected ones and the unselected ones before it
+        p.kv_idx[row + (c == 1 ? bp : n_part + (kb - bp))] = kb;
+        p.fkv_idx[row + (c == 2 ? bf : n_full + (kb - bf))] = kb;
+      }
+      seen_part += tp;
+      seen_full += tf;
+    }
+    n_part = seen_part;
+    n_full = seen_full;
   }
   if (threadIdx.x == 0) {
     p.kv_num[qb] = n_part;
     p.fkv_num[qb] = n_full;
-  }
-
-  // pass 2: slots.  A selected kv-block goes after the selected ones before
-  // it; an unselected one goes after all selected ones and the unselected
-  // ones before it.
-  int seen_part = 0, seen_full = 0;
-  for (int base = 0; base < nk; base += kThreads) {
-    const int kb = base + threadIdx.x;
-    const int c = kb < nk ? classify(p, qb, kb) : 0;
-    int tp, tf;
-    const int bp = seen_part + block_prefix(c == 1, wave_tot, &tp);
-    const int bf = seen_full + block_prefix(c == 2, wave_tot, &tf);
-    if (kb < nk) {
-      p.kv_idx[row + (c == 1 ? bp : n_part + (kb - bp))] = kb;
-      p.fkv_idx[row + (c == 2 ? bf : n_full + (kb - bf))] = kb;
-    }
-    seen_part += tp;
-    seen_full += tf;
   }
 }
 

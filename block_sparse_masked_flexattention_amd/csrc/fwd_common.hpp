@@ -1,0 +1,90 @@
+// fwd_common.hpp -- pieces shared by the bf16 and fp32 forward kernels.
+#pragma once
+#include "internal.hpp"
+
+namespace flexattn {
+namespace fwd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kLdsBytes = 160 * 1024;
+
+// value of lane l ^ 32
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
+
+// max over lanes l and l ^ 32, in every lane: v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second.
+__device__ inline float max_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline u32x4 ld_global16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// swap bits 2 and 3 of a row index (an involution)
+__device__ inline int swap23(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Work-group -> (head bh, q-block qb).  Work-groups are dispatched round-robin
+// over the 8 XCDs; the remap gives each XCD a contiguous range of (head,
+// q-block) work so a head's K/V stay in that XCD's L2.  Within a head the
+// q-blocks run last-to-first, the heaviest first under a causal-like mask.
+__device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
+  const int nwg = gridDim.x, w = blockIdx.x;
+  const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
+  const int r = xcd * per + min(xcd, rem) + (w >> 3);
+  bh = r / n_qb;
+  qb = n_qb - 1 - (r - bh * n_qb);
+}
+
+// Keys visible from query row qi, as one interval [lo, hi] (empty when
+// lo > hi), already clipped to the key range.
+template <int MASK>
+__device__ inline void row_interval(const FwdParams& p, int qi, int& lo, int& hi) {
+  lo = 0;
+  hi = p.kv_len - 1;
+  if constexpr (MASK == FLEX_MASK_CAUSAL) {
+    hi = min(hi, qi);
+  } else if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) {
+    lo = max(0, qi - p.window);
+    hi = min(hi, qi - p.window_min);
+  } else if constexpr (MASK == FLEX_MASK_PREFIX_CAUSAL) {
+    hi = min(hi, qi <= p.prefix ? max(p.prefix, qi) : qi);
+  }
+}
+
+// Store one query row of O^T accumulators (lane half g) scaled by inv.
+// Accumulator register r of column block e holds d = 32e + 8(r/4) + 4g + r%4.
+template <int NE>
+__device__ inline void write_out_row(const FwdParams& p, size_t row, int D, int g,
+                                     const f32x16 (&o)[NE], float inv) {
+  char* og = static_cast<char*>(p.out) + row * (size_t)D * (p.out_bf16 ? 2 : 4);
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d = 32 * e + 8 * a + 4 * g;
+      const float v0 = o[e][4 * a] * inv, v1 = o[e][4 * a + 1] * inv;
+      const float v2 = o[e][4 * a + 2] * inv, v3 = o[e][4 * a + 3] * inv;
+      if (p.out_bf16) {
+        *reinterpret_cast<bf16x4*>(og + d * 2) =
+            bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+      } else {
+        *reinterpret_cast<f32x4*>(og + d * 4) = f32x4{v0, v1, v2, v3};
+      }
+    }
+}
+
+}  // namespace fwd
+}  // namespace flexattn
