@@ -35,9 +35,11 @@
 //    computes; one barrier per step.  The buffers are distinct LDS variables
 //    and the step loop is unrolled by two, so the compiler can tell the
 //    loads' destination from the buffer being read.
-//  * Inside a step the keys go through in 32-key blocks: the next block's
-//    S^T products are issued before the current block's softmax, so matrix
-//    and vector work overlap, and only one block of scores is live.
+//  * Inside a step the keys go through in 32-key blocks (S^T, softmax, P V),
+//    so only one block of scores is live and four waves fit on each SIMD;
+//    the waves' matrix and vector work interleave on the SIMD.  (Issuing the
+//    next block's S^T products ahead of the current softmax was measured
+//    slower: its extra live registers either drop a wave per SIMD or spill.)
 //  * Scores live in base-2 units (scale * log2 e folded into one FMA) and go
 //    through v_exp_f32.  The running max used for exponentiation is only
 //    raised when a row's max exceeds it by more than 2^8 (probabilities then
@@ -92,6 +94,13 @@ struct Bf16Fwd {
   static constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
   static constexpr int NDMA = KS * CPR / (64 * NW);  // 16-byte loads per lane per step (K or V)
   static constexpr float TAU = 8.0f;         // lazy-rescale threshold (log2 units)
+  // Occupancy the register allocation aims for, in waves per SIMD: 4 for
+  // head dim 64 (<= 128 VGPRs), 2 for 128, and never more than the LDS
+  // allows (two stage buffers of K and V per work-group, 160 KiB per CU).
+  static constexpr int LDS_WAVES = (kLdsBytes / (4 * STAGE)) * NW / 4;
+  static constexpr int REG_WAVES = D == 64 ? 4 : 2;
+  static constexpr int WAVES_PER_SIMD =
+      LDS_WAVES < 1 ? 1 : (LDS_WAVES < REG_WAVES ? LDS_WAVES : REG_WAVES);
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
   static_assert(D == 64 || D == 128, "head dim");
 
@@ -172,11 +181,15 @@ struct Bf16Fwd {
     const int np = min(max(p.kv_num[qb], 0), nk);
     const int nf = min(max(p.fkv_num[qb], 0), nk);
     const int nsteps = (np + nf) * SPT;
-    const int32_t* prow = p.kv_idx + (size_t)qb * nk;
-    const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
+    // the index rows are read-only for the kernel's lifetime: reading them
+    // through the constant address space makes the loads scalar (s_load via
+    // the scalar cache) rather than a vector load waited on at once
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    const cint32* prow = (const cint32*)(p.kv_idx + (size_t)qb * nk);
+    const cint32* frow = (const cint32*)(p.fkv_idx + (size_t)qb * nk);
     auto tile_kb = [&](int t) {
       const int v = t < np ? prow[t] : frow[t - np];
-      return __builtin_amdgcn_readfirstlane(min(max(v, 0), nk - 1));
+      return min(max(v, 0), nk - 1);
     };
 
     // Load step (kb, part) into a stage buffer: K and V, 16 bytes per lane
@@ -224,22 +237,34 @@ struct Bf16Fwd {
 
     // S^T block b (32 keys) of the step in `cur`, for every query sub-tile
     auto s_block = [&](const lds_t* cur, int b, f32x16 (&s)[NQ]) {
+      u32x4 kf[D / 16];  // all K fragments of the block in flight at once
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) kf[t] = FLEXATTN_LDS(u32x4, cur + kro[t] + 32 * b * ROWB);
 #pragma unroll
       for (int c = 0; c < NQ; ++c) s[c] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const u32x4 kf = FLEXATTN_LDS(u32x4, cur + kro[t] + 32 * b * ROWB);
+      for (int t = 0; t < D / 16; ++t)
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
           s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[c][t]), s[c], 0,
-              0, 0);
-      }
+              __builtin_bit_cast(bf16x8, kf[t]), __builtin_bit_cast(bf16x8, qf[c][t]), s[c],
+              0, 0, 0);
+    };
+    // V^T fragments of block b, half hh, column block e (two transposing reads)
+    auto v_frag = [&](const lds_t* cur, int b, int hh, int e) {
+      const lds_t* vp = cur + vro[e] + (32 * b + 16 * hh) * ROWB;
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)vp);
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vp + 4 * ROWB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
     // One step: everything reads buf[BUF]; the next step is loaded into the
-    // other buffer meanwhile.
-    int kb_cur = 0;
+    // other buffer meanwhile.  Tile indices are fetched one tile ahead of
+    // their use so that their load latency hides behind a whole tile.
+    const int ntiles = np + nf;
+    int kb_cur = 0, kb_nxt = 0;
     auto step = [&](auto buf_tag, int n) {
       constexpr int BUF = decltype(buf_tag)::value;
       lds_t* cur = buf[BUF];
@@ -247,21 +272,26 @@ struct Bf16Fwd {
       const int kv0 = kb_cur * KB + part * KS;
       // a listed-full tile at a ragged edge is still handled as partial
       const bool partial = t < np || q_ragged || kb_cur * KB + KB > p.kv_len;
-      int kb_next = kb_cur;
-      if (n + 1 < nsteps) {
-        const int tn = (n + 1) / SPT;
-        if (tn != t) kb_next = tile_kb(tn);
-        dma(buf[BUF ^ 1], kb_next, (n + 1) % SPT);
-      }
+      const bool last_part = part == SPT - 1;
+      if (n + 1 < nsteps) dma(buf[BUF ^ 1], last_part ? kb_nxt : kb_cur, (n + 1) % SPT);
+      int kb_after = kb_nxt;
+      if (last_part && t + 2 < ntiles) kb_after = tile_kb(t + 2);
 
-      f32x16 s_nxt[NQ];
-      s_block(cur, 0, s_nxt);
 #pragma unroll
       for (int b = 0; b < NBS; ++b) {
-        f32x16 s[NQ];
+        // On a partial tile, skip a 32-key block that no row of this wave
+        // sees: its scores would all be -inf, i.e. weight exactly 0 and no
+        // change to the running max.  (Diagonal tiles of a causal mask and
+        // the window edges are mostly such blocks.)
+        if (partial) {
+          const int b0 = kv0 + 32 * b;
+          bool any = false;
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) s[c] = s_nxt[c];
-        if (b + 1 < NBS) s_block(cur, b + 1, s_nxt);
+          for (int c = 0; c < NQ; ++c) any |= lo[c] <= b0 + 31 && hi[c] >= b0 && lo[c] <= hi[c];
+          if (!__any(any)) continue;
+        }
+        f32x16 s[NQ];
+        s_block(cur, b, s);
 
         // score modification, mask and running max; register r holds key
         // kv0 + 32b + 8g + 16(r >> 3) + (r & 7)
@@ -288,9 +318,13 @@ struct Bf16Fwd {
               s[c][r] = vis ? s[c][r] : -INFINITY;
             }
           }
-          float mx = fmaxf(s[c][0], s[c][1]);
-#pragma unroll
-          for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[c][r], s[c][r + 1]));
+          // 16-way max as a v_max3 tree: 8 instructions, depth 3
+          const float t0 = max3(s[c][0], s[c][1], s[c][2]);
+          const float t1 = max3(s[c][3], s[c][4], s[c][5]);
+          const float t2 = max3(s[c][6], s[c][7], s[c][8]);
+          const float t3 = max3(s[c][9], s[c][10], s[c][11]);
+          const float t4 = max3(s[c][12], s[c][13], s[c][14]);
+          float mx = fmaxf(max3(t0, t1, t2), max3(t3, t4, s[c][15]));
           mx = max_halves(mx);
           if constexpr (SCORE == FLEX_SCORE_IDENTITY) mx *= c1;
           // raise the running max only when this block's max exceeds it by
@@ -302,26 +336,39 @@ struct Bf16Fwd {
         }
         const bool rescale = __any(need_any);  // wave-uniform
 
+        // the block's V^T fragments go out before the exponentials
+        bf16x8 vf[NE][2];
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) vf[e][hh] = v_frag(cur, b, hh, e);
+
         bf16x8 pk[NQ][2];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
           // rows with nothing visible yet keep m = -inf; exponentiate against 0
           const float m_use = (partial && m_run[c] == -INFINITY) ? 0.f : m_run[c];
-          float rowsum = 0.f;
+          float pv[16];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (SCORE == FLEX_SCORE_IDENTITY)
+              pv[r] = __builtin_amdgcn_exp2f(fmaf(s[c][r], c1, -m_use));
+            else
+              pv[r] = __builtin_amdgcn_exp2f(s[c][r] - m_use);
+          }
+          float rowsum = pv[0];  // fp32 sum: the LSE needs ~1e-4 relative accuracy
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float x = s[c][8 * hh + i];
-              float pv;
-              if constexpr (SCORE == FLEX_SCORE_IDENTITY)
-                pv = __builtin_amdgcn_exp2f(fmaf(x, c1, -m_use));
-              else
-                pv = __builtin_amdgcn_exp2f(x - m_use);
-              rowsum += pv;
-              pk[c][hh][i] = (__bf16)pv;
-            }
-          l_run[c] = l_run[c] * alpha[c] + rowsum;
+          for (int r = 1; r < 16; ++r) rowsum += pv[r];
+          l_run[c] = fmaf(l_run[c], alpha[c], rowsum);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            unsigned w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              w[i] = __builtin_bit_cast(
+                  unsigned, bf16x2{(__bf16)pv[8 * hh + 2 * i], (__bf16)pv[8 * hh + 2 * i + 1]});
+            pk[c][hh] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+          }
         }
 
         // O^T += V^T P^T; the alpha rescale first (per D-half with SUB)
@@ -338,27 +385,23 @@ struct Bf16Fwd {
 #pragma unroll
           for (int e = half * EPH; e < (half + 1) * EPH; ++e)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const lds_t* vp = cur + vro[e] + (32 * b + 16 * hh) * ROWB;
-              const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4*)vp);
-              const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4*)(vp + 4 * ROWB));
-              const bf16x8 vf = __builtin_bit_cast(
-                  bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
               for (int c = 0; c < NQ; ++c)
-                o[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[c][hh], o[c][e], 0,
-                                                                  0, 0);
-            }
+                o[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[e][hh], pk[c][hh],
+                                                                  o[c][e], 0, 0, 0);
         }
       }
       __syncthreads();  // the next step's loads have landed; this buffer is free
-      kb_cur = kb_next;
+      if (last_part) {
+        kb_cur = kb_nxt;
+        kb_nxt = kb_after;
+      }
     };
 
     if (nsteps > 0) {
       kb_cur = tile_kb(0);
+      if (ntiles > 1) kb_nxt = tile_kb(1);
       dma(buf[0], kb_cur, 0);
     }
     __syncthreads();

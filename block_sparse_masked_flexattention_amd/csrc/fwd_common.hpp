@@ -7,6 +7,7 @@ namespace fwd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -27,6 +28,12 @@ __device__ inline float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Three-input max; with NaNs not honoured the compiler emits one v_max3_f32.
+// (Plain C rather than inline assembly: the compiler must see the
+// instruction to insert the wait states a VALU read of a matrix-instruction
+// result needs.)
+__device__ inline float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 __device__ inline u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -37,13 +44,28 @@ __device__ inline int swap23(int m) {
 }
 
 // Work-group -> (head bh, q-block qb).  Work-groups are dispatched round-robin
-// over the 8 XCDs; the remap gives each XCD a contiguous range of (head,
-// q-block) work so a head's K/V stay in that XCD's L2.  Within a head the
-// q-blocks run last-to-first, the heaviest first under a causal-like mask.
+// over the 8 XCDs (work-group w to XCD w % 8), and each XCD has its own L2.
+//  * When the number of heads is a multiple of 8, XCD x owns heads
+//    [x H/8, (x+1) H/8) and runs their q-blocks last-to-first across all of
+//    them: every head's last q-block, then every head's second-to-last, ...
+//    Under a causal-like mask the last q-blocks are the longest, so long work
+//    starts first and the short blocks fill the tail, while each head's K/V
+//    stay in one XCD's L2.
+//  * Otherwise each XCD gets a contiguous range of (head, q-block) work,
+//    q-blocks last-to-first within a head.
 __device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
   const int nwg = gridDim.x, w = blockIdx.x;
-  const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
-  const int r = xcd * per + min(xcd, rem) + (w >> 3);
+  const int n_heads = nwg / n_qb;
+  const int xcd = w & 7, k = w >> 3;
+  if ((n_heads & 7) == 0) {
+    const int hx = n_heads >> 3;
+    const int rank = k / hx;
+    bh = xcd * hx + (k - rank * hx);
+    qb = n_qb - 1 - rank;
+    return;
+  }
+  const int per = nwg >> 3, rem = nwg & 7;
+  const int r = xcd * per + min(xcd, rem) + k;
   bh = r / n_qb;
   qb = n_qb - 1 - (r - bh * n_qb);
 }

@@ -13,8 +13,9 @@ namespace fwd {
 // (the clang attribute rather than the __launch_bounds__ macro: template
 // arguments carry commas)
 template <int D, int QB, int KB, int MASK, int SCORE, bool SUB>
-__global__ __attribute__((amdgpu_flat_work_group_size(
-    1, Bf16Fwd<D, QB, KB, MASK, SCORE, SUB>::NT))) void bf16_fwd_kernel(FwdParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16Fwd<D, QB, KB, MASK, SCORE, SUB>::NT),
+                          amdgpu_waves_per_eu(Bf16Fwd<D, QB, KB, MASK, SCORE, SUB>::WAVES_PER_SIMD)))
+void bf16_fwd_kernel(FwdParams p) {
   Bf16Fwd<D, QB, KB, MASK, SCORE, SUB>::run(p);
 }
 
