@@ -41,12 +41,21 @@
 //    next block's S^T products ahead of the current softmax was measured
 //    slower: its extra live registers either drop a wave per SIMD or spill.)
 //  * Scores live in base-2 units (scale * log2 e folded into one FMA) and go
-//    through v_exp_f32.  The running max used for exponentiation is only
-//    raised when a row's max exceeds it by more than 2^8 (probabilities then
-//    stay <= 256, exact in bf16's exponent range), so the accumulator rescale
-//    runs only on tiles where some row of the wave needs it; the final
-//    out = acc / l and lse = m + log2 l use that same max, so the result is
-//    the softmax of the scores up to rounding.
+//    through v_exp_f32.  Probabilities are taken against a per-row offset m
+//    that may lag the row max: a block first exponentiates against the
+//    current m and sums; only when some lane's sum exceeds 2^16 (a score rose
+//    by more than 16 above m) or a row meets its first visible key does the
+//    wave take the slow path, recompute the block's scores, raise m to the
+//    block max, rescale the accumulator and row sum by alpha and
+//    exponentiate again.  Most blocks thus cost no max reduction and no
+//    rescale; out = acc / l and lse = m + log2 l use the same m, so the
+//    result is the softmax of the scores up to rounding.
+//  * The relative-position bias is linear in q - kv, so it enters as the
+//    initial value of the S^T accumulators (two chains of adds of a uniform
+//    step) and costs nothing per score after the product.
+//  * s_setprio raises the wave's issue priority while it issues matrix
+//    instructions, so a wave ready for the matrix unit goes ahead of the
+//    other waves' vector work.
 //  * For every supported mask kind the keys a query row sees form one
 //    interval; it is computed once per row (the q-side predicate hoisted out
 //    of the key loop, as the templated-attention performance issue did by
@@ -80,12 +89,40 @@ struct Int {
   static constexpr int value = V;
 };
 
+// Keys per step (one LDS stage) and number of stage buffers.  A step's K and
+// V arrive NSTAGE - 1 steps ahead of their use.
+template <int D, int QB, int KB>
+constexpr int bf16_ks() {
+#ifdef FLEXATTN_KS
+  return FLEXATTN_KS;
+#else
+  return 64;
+#endif
+}
+template <int D, int QB, int KB>
+constexpr int bf16_nstage() {
+#ifdef FLEXATTN_NSTAGE
+  return FLEXATTN_NSTAGE;
+#else
+  return 2;
+#endif
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int D, int QB, int KB, int MASK, int SCORE, bool SUB>
 struct Bf16Fwd {
   static constexpr int NQ = bf16_nq<D, QB, KB>();
   static constexpr int NW = QB / (32 * NQ);  // waves per work-group
   static constexpr int NT = 64 * NW;         // threads per work-group
-  static constexpr int KS = 64;              // keys per step (one LDS stage)
+  static constexpr int KS = bf16_ks<D, QB, KB>();          // keys per step
+  static constexpr int NSTAGE = bf16_nstage<D, QB, KB>();  // LDS stage buffers
   static constexpr int SPT = KB / KS;        // steps per block-mask tile
   static constexpr int NBS = KS / 32;        // 32-key blocks per step
   static constexpr int NE = D / 32;          // 32-column blocks of the head dim
@@ -93,16 +130,26 @@ struct Bf16Fwd {
   static constexpr int STAGE = KS * ROWB;    // bytes of K (or V) per step
   static constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
   static constexpr int NDMA = KS * CPR / (64 * NW);  // 16-byte loads per lane per step (K or V)
-  static constexpr float TAU = 8.0f;         // lazy-rescale threshold (log2 units)
+  static constexpr int DMA_PER_STEP = 2 * NDMA;      // vector-memory instructions per step
+  // Probabilities are taken against a running offset that may lag the row
+  // max; a block whose probabilities would exceed kPMax raises it.
+  static constexpr float kPMax = 65536.0f;
   // Occupancy the register allocation aims for, in waves per SIMD: 4 for
   // head dim 64 (<= 128 VGPRs), 2 for 128, and never more than the LDS
-  // allows (two stage buffers of K and V per work-group, 160 KiB per CU).
-  static constexpr int LDS_WAVES = (kLdsBytes / (4 * STAGE)) * NW / 4;
+  // allows (NSTAGE stage buffers of K and V per work-group, 160 KiB per CU).
+  static constexpr int LDS_WAVES = (kLdsBytes / (NSTAGE * 2 * STAGE)) * NW / 4;
+#ifdef FLEXATTN_WAVES
+  static constexpr int REG_WAVES = FLEXATTN_WAVES;
+#else
   static constexpr int REG_WAVES = D == 64 ? 4 : 2;
+#endif
   static constexpr int WAVES_PER_SIMD =
       LDS_WAVES < 1 ? 1 : (LDS_WAVES < REG_WAVES ? LDS_WAVES : REG_WAVES);
+  static_assert(KS == 32 || KS == 64, "step size");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stage count");
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert((NSTAGE - 2) * DMA_PER_STEP < 64, "vmcnt range");
 
   // K: row m, 16-byte chunk c at chunk c ^ kswz(m)
   __device__ static inline int kswz(int m) {
@@ -114,10 +161,43 @@ struct Bf16Fwd {
                    : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)));
   }
 
+  // pairwise sum of 16 values (depth 4)
+  __device__ static inline float sum16(const float (&x)[16]) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = x[2 * i] + x[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  }
+
+  // End of a step: this wave's loads for the next step are complete (those
+  // of later steps may stay in flight: `later` of them were issued), then
+  // the work-group barrier.  The empty asm statements keep the compiler from
+  // moving memory accesses across the barrier.
+  __device__ static inline void step_barrier(int later) {
+    if constexpr (NSTAGE >= 4) {
+      if (later >= 2) wait_vmcnt<2 * DMA_PER_STEP>();
+      else if (later == 1) wait_vmcnt<DMA_PER_STEP>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NSTAGE == 3) {
+      if (later >= 1) wait_vmcnt<DMA_PER_STEP>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
   __device__ static void run(const FwdParams& p) {
-    __shared__ __attribute__((aligned(16))) char sbuf0[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) char sbuf1[2 * STAGE];
-    lds_t* const buf[2] = {(lds_t*)sbuf0, (lds_t*)sbuf1};
+    // one distinct LDS variable per stage buffer (unused ones are tiny)
+    __shared__ __attribute__((aligned(16))) char sb0[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char sb1[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char sb2[NSTAGE > 2 ? 2 * STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char sb3[NSTAGE > 3 ? 2 * STAGE : 16];
+    lds_t* const buf[4] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,49 +251,67 @@ struct Bf16Fwd {
 #pragma unroll
     for (int c = 0; c < NQ; ++c) row_interval<MASK>(p, qi[c], lo[c], hi[c]);
 
-    float nsl2 = 0.f;  // -slope_h * log2(e)
-    if constexpr (SCORE == FLEX_SCORE_REL_BIAS)
-      nsl2 = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) * kLog2e;
     const float c1 = p.c1;
+    // Relative bias -slope_h (q - kv) in units of the raw score (c1 s + bias
+    // in base 2 = c1 (s + bias / (|scale| ln 2 log2 e))): bias_u per unit
+    // of q - kv.
+    float bias_u = 0.f, bias_u16 = 0.f;
+    if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * kLn2);
+      bias_u16 = 16.0f * bias_u;
+    }
 
-    // ---- step list: tile n / SPT, part n % SPT ----
+    // ---- tile list: partial tiles, then full tiles ----
     const int nk = p.n_kb;
     const int np = min(max(p.kv_num[qb], 0), nk);
     const int nf = min(max(p.fkv_num[qb], 0), nk);
-    const int nsteps = (np + nf) * SPT;
-    // the index rows are read-only for the kernel's lifetime: reading them
-    // through the constant address space makes the loads scalar (s_load via
-    // the scalar cache) rather than a vector load waited on at once
-    typedef __attribute__((address_space(4))) const int32_t cint32;
-    const cint32* prow = (const cint32*)(p.kv_idx + (size_t)qb * nk);
-    const cint32* frow = (const cint32*)(p.fkv_idx + (size_t)qb * nk);
-    auto tile_kb = [&](int t) {
-      const int v = t < np ? prow[t] : frow[t - np];
+    const int ntiles = np + nf;
+    const int nsteps = ntiles * SPT;
+    const int32_t* prow = p.kv_idx + (size_t)qb * nk;
+    const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
+    // Tile indices 64 at a time: lane i of `win` holds the kv-block of tile
+    // win_base + i, lane i of `win_nx` that of tile win_base + 64 + i; a
+    // tile's index is then one v_readlane.  The next window is loaded 64
+    // tiles ahead of its use.
+    auto load_window = [&](int base) {  // raw values; clamped when read
+      const int t = min(base + lane, ntiles - 1);
+      int v = 0;
+      if (t >= 0) v = t < np ? prow[t] : frow[t - np];
+      return v;
+    };
+    int win_base = 0;
+    int win = load_window(0);
+    int win_nx = ntiles > 64 ? load_window(64) : 0;
+    auto tile_kb = [&](int t) {  // t in [win_base, win_base + 128)
+      const int i = t - win_base;
+      const int v = i < 64 ? __builtin_amdgcn_readlane(win, i)
+                           : __builtin_amdgcn_readlane(win_nx, i - 64);
       return min(max(v, 0), nk - 1);
     };
 
-    // Load step (kb, part) into a stage buffer: K and V, 16 bytes per lane
-    // per instruction straight into LDS.  The instruction's LDS slot for lane
-    // i is fixed (base + 16 i), so the swizzle is applied on the global side:
-    // slot s = (row m, position q) receives K row swap23(m), chunk q ^ kswz(m)
-    // and V row m, chunk q ^ vswz(m) / 2.  Rows past the end of the keys are
-    // clamped to the last key; the mask gives them zero weight.
-    auto dma = [&](lds_t* dst, int kb, int part) {
+    // Load step m into a stage buffer: K and V, 16 bytes per lane per
+    // instruction straight into LDS.  The instruction's LDS slot for lane i
+    // is fixed (base + 16 i), so the swizzle is applied on the global side:
+    // slot s = (row r, position q) receives K row swap23(r), chunk
+    // q ^ kswz(r) and V row r, chunk q ^ vswz(r) / 2.  Rows past the end of
+    // the keys are clamped to the last key; the mask gives them zero weight.
+    auto dma = [&](lds_t* dst, int m) {
+      const int kb = tile_kb(m / SPT);
       // a step may start past the last key (second half of a short ragged
       // tile): then every row reads the last key
-      const int kv0 = min(kb * KB + part * KS, p.kv_len - 1);
+      const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
       const int rows_left = min(KS, p.kv_len - kv0);  // >= 1
       const char* kt = kg + (size_t)kv0 * ROWB;
       const char* vt = vg + (size_t)kv0 * ROWB;
 #pragma unroll
       for (int j = 0; j < NDMA; ++j) {
         const int sl = (wave * NDMA + j) * 64 + lane;
-        const int m = sl / CPR, q = sl % CPR;
-        const int mk = min((m & ~31) | swap23(m & 31), rows_left - 1);
-        const int mv = min(m, rows_left - 1);
+        const int r = sl / CPR, q = sl % CPR;
+        const int rk = min((r & ~31) | swap23(r & 31), rows_left - 1);
+        const int rv = min(r, rows_left - 1);
         // 32-bit unsigned offsets from a uniform base: the SGPR-base form
-        const unsigned ko = (unsigned)(mk * ROWB) + ((unsigned)(q ^ kswz(m)) << 4);
-        const unsigned vo = (unsigned)(mv * ROWB) + ((unsigned)(q ^ (vswz(m) >> 1)) << 4);
+        const unsigned ko = (unsigned)(rk * ROWB) + ((unsigned)(q ^ kswz(r)) << 4);
+        const unsigned vo = (unsigned)(rv * ROWB) + ((unsigned)(q ^ (vswz(r) >> 1)) << 4);
         __builtin_amdgcn_global_load_lds(kt + ko,
                                          (__attribute__((address_space(3))) void*)(
                                              dst + (wave * NDMA + j) * 1024),
@@ -225,23 +323,51 @@ struct Bf16Fwd {
       }
     };
 
-    float m_run[NQ], l_run[NQ];
+    // Running state per query row: m_run is the offset the probabilities
+    // are taken against (a lower bound of the row max, in base-2 units),
+    // nm = -m_run (+inf before the row's first visible key), l_run the sum
+    // of probabilities (per lane half), o the output accumulator.
+    float m_run[NQ], nm[NQ], l_run[NQ];
     f32x16 o[NQ][NE];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       m_run[c] = -INFINITY;
+      nm[c] = INFINITY;
       l_run[c] = 0.f;
 #pragma unroll
       for (int e = 0; e < NE; ++e) o[c][e] = f32x16{};
     }
 
-    // S^T block b (32 keys) of the step in `cur`, for every query sub-tile
-    auto s_block = [&](const lds_t* cur, int b, f32x16 (&s)[NQ]) {
+    // S^T block b (32 keys) of the step in `cur`, for every query sub-tile,
+    // keys from kvl on (register r: key kvl + 16(r >> 3) + (r & 7)).  With
+    // the relative bias the accumulators start at bias / c1, so that the
+    // product leaves c1 s + bias in one FMA, as for the plain score.
+    auto s_block = [&](const lds_t* cur, int b, int kvl, f32x16 (&s)[NQ]) {
       u32x4 kf[D / 16];  // all K fragments of the block in flight at once
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) kf[t] = FLEXATTN_LDS(u32x4, cur + kro[t] + 32 * b * ROWB);
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) s[c] = f32x16{};
+      for (int c = 0; c < NQ; ++c) {
+        if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+          // bias_u (q - kv) for keys kvl + r and kvl + 16 + r, r < 8, as two
+          // chains of -bias_u steps (no per-register constants).  The empty
+          // asm statement keeps the compiler from carrying one call's values
+          // over to the next call in registers.
+          float a = bias_u * (float)(qi[c] - kvl);
+          asm volatile("" : "+v"(a));
+          float x = a, y = a - bias_u16;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            s[c][r] = x;
+            s[c][8 + r] = y;
+            x -= bias_u;
+            y -= bias_u;
+          }
+        } else {
+          s[c] = f32x16{};
+        }
+      }
+      __builtin_amdgcn_s_setprio(1);  // keep the matrix unit fed first
 #pragma unroll
       for (int t = 0; t < D / 16; ++t)
 #pragma unroll
@@ -249,6 +375,7 @@ struct Bf16Fwd {
           s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8, kf[t]), __builtin_bit_cast(bf16x8, qf[c][t]), s[c],
               0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     };
     // V^T fragments of block b, half hh, column block e (two transposing reads)
     auto v_frag = [&](const lds_t* cur, int b, int hh, int e) {
@@ -260,22 +387,44 @@ struct Bf16Fwd {
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // One step: everything reads buf[BUF]; the next step is loaded into the
-    // other buffer meanwhile.  Tile indices are fetched one tile ahead of
-    // their use so that their load latency hides behind a whole tile.
-    const int ntiles = np + nf;
-    int kb_cur = 0, kb_nxt = 0;
+    // p = 2^(c1 s + offset)
+    auto exp_score = [&](float sc, float nmc) { return __builtin_amdgcn_exp2f(fmaf(sc, c1, nmc)); };
+    // set the keys row c does not see (partial tiles) to `fill`
+    auto mask_block = [&](auto& x, int c, int kvl, float fill) {
+      const int lim_hi = hi[c] - kvl, lim_lo = lo[c] - kvl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 16 * (r >> 3) + (r & 7);
+        bool vis = off <= lim_hi;
+        if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) vis = vis && off >= lim_lo;
+        x[r] = vis ? x[r] : fill;
+      }
+    };
+
+    // One step: everything reads buf[B]; step n + NSTAGE - 1 is loaded into
+    // the buffer step n - 1 used.
     auto step = [&](auto buf_tag, int n) {
-      constexpr int BUF = decltype(buf_tag)::value;
-      lds_t* cur = buf[BUF];
+      constexpr int B = decltype(buf_tag)::value;
+      lds_t* cur = buf[B];
       const int t = n / SPT, part = n % SPT;
-      const int kv0 = kb_cur * KB + part * KS;
+      if (t >= win_base + 64) {  // slide the index window
+        win_base += 64;
+        win = win_nx;
+        if (win_base + 64 < ntiles) win_nx = load_window(win_base + 64);
+      }
+      const int kb = tile_kb(t);
+      const int kv0 = kb * KB + part * KS;
       // a listed-full tile at a ragged edge is still handled as partial
-      const bool partial = t < np || q_ragged || kb_cur * KB + KB > p.kv_len;
-      const bool last_part = part == SPT - 1;
-      if (n + 1 < nsteps) dma(buf[BUF ^ 1], last_part ? kb_nxt : kb_cur, (n + 1) % SPT);
-      int kb_after = kb_nxt;
-      if (last_part && t + 2 < ntiles) kb_after = tile_kb(t + 2);
+      const bool partial = t < np || q_ragged || kb * KB + KB > p.kv_len;
+      // With more than two buffers every step issues the same loads (past
+      // the last step it reloads the last one into a buffer nobody reads),
+      // so the compiler can count them and wait only for the buffer being
+      // read.  With two, each barrier waits for everything anyway.
+      if constexpr (NSTAGE == 2) {
+        if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
+      } else {
+        dma(buf[(B + NSTAGE - 1) % NSTAGE], min(n + NSTAGE - 1, nsteps - 1));
+      }
 
 #pragma unroll
       for (int b = 0; b < NBS; ++b) {
@@ -290,51 +439,10 @@ struct Bf16Fwd {
           for (int c = 0; c < NQ; ++c) any |= lo[c] <= b0 + 31 && hi[c] >= b0 && lo[c] <= hi[c];
           if (!__any(any)) continue;
         }
-        f32x16 s[NQ];
-        s_block(cur, b, s);
-
-        // score modification, mask and running max; register r holds key
-        // kv0 + 32b + 8g + 16(r >> 3) + (r & 7)
+        // register r holds key kvl + 16(r >> 3) + (r & 7)
         const int kvl = kv0 + 32 * b + 8 * g;
-        float alpha[NQ];
-        bool need_any = false;
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-          if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
-            const float bias0 = nsl2 * (float)(qi[c] - kvl);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int off = 16 * (r >> 3) + (r & 7);
-              s[c][r] = fmaf(s[c][r], c1, fmaf(-nsl2, (float)off, bias0));
-            }
-          }
-          if (partial) {
-            const int lim_hi = hi[c] - kvl, lim_lo = lo[c] - kvl;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int off = 16 * (r >> 3) + (r & 7);
-              bool vis = off <= lim_hi;
-              if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) vis = vis && off >= lim_lo;
-              s[c][r] = vis ? s[c][r] : -INFINITY;
-            }
-          }
-          // 16-way max as a v_max3 tree: 8 instructions, depth 3
-          const float t0 = max3(s[c][0], s[c][1], s[c][2]);
-          const float t1 = max3(s[c][3], s[c][4], s[c][5]);
-          const float t2 = max3(s[c][6], s[c][7], s[c][8]);
-          const float t3 = max3(s[c][9], s[c][10], s[c][11]);
-          const float t4 = max3(s[c][12], s[c][13], s[c][14]);
-          float mx = fmaxf(max3(t0, t1, t2), max3(t3, t4, s[c][15]));
-          mx = max_halves(mx);
-          if constexpr (SCORE == FLEX_SCORE_IDENTITY) mx *= c1;
-          // raise the running max only when this block's max exceeds it by
-          // more than TAU; alpha is exactly 1 otherwise (also at -inf)
-          const bool need = mx > m_run[c] + TAU;
-          alpha[c] = need ? __builtin_amdgcn_exp2f(m_run[c] - mx) : 1.0f;
-          if (need) m_run[c] = mx;
-          need_any |= need;
-        }
-        const bool rescale = __any(need_any);  // wave-uniform
+        f32x16 s[NQ];
+        s_block(cur, b, kvl, s);
 
         // the block's V^T fragments go out before the exponentials
         bf16x8 vf[NE][2];
@@ -343,30 +451,69 @@ struct Bf16Fwd {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) vf[e][hh] = v_frag(cur, b, hh, e);
 
+        // Fast path: exponentiate against the stored offset, zero the masked
+        // keys, and check that every probability stayed below kPMax (a row
+        // that has not seen a key yet has offset +inf, so a visible key
+        // gives +inf and fails the check).
+        float pv[NQ][16], rs[NQ];
+        bool bad = false;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm[c]);
+          if (partial) mask_block(pv[c], c, kvl, 0.f);
+          rs[c] = sum16(pv[c]);
+          bad |= rs[c] > kPMax;
+        }
+        float alpha[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) alpha[c] = 1.0f;
+        const bool rescale = __any(bad);  // wave-uniform
+        if (rescale) {
+          // Slow path (a row's first visible keys, or scores that rose by
+          // more than log2 kPMax): recompute the block's scores, raise the
+          // running max of every row of the wave to the block max, rescale
+          // by alpha and exponentiate again.  (The empty asm statement
+          // makes the compiler read K from LDS again instead of keeping the
+          // fast path's fragments live through it.)
+          asm volatile("" ::: "memory");
+          s_block(cur, b, kvl, s);
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) {
+            if (partial) mask_block(s[c], c, kvl, -INFINITY);
+            // 16-way max as a v_max3 tree: 8 instructions, depth 3
+            const float t0 = max3(s[c][0], s[c][1], s[c][2]);
+            const float t1 = max3(s[c][3], s[c][4], s[c][5]);
+            const float t2 = max3(s[c][6], s[c][7], s[c][8]);
+            const float t3 = max3(s[c][9], s[c][10], s[c][11]);
+            const float t4 = max3(s[c][12], s[c][13], s[c][14]);
+            float mx = fmaxf(max3(t0, t1, t2), max3(t3, t4, s[c][15]));
+            mx = max_halves(mx) * c1;
+            const float m_new = fmaxf(m_run[c], mx);
+            const bool seen = m_new != -INFINITY;
+            // rows still at -inf keep alpha = 1 (their sum and output are 0)
+            alpha[c] = seen ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.0f;
+            m_run[c] = m_new;
+            // masked scores are -inf here, so a finite offset zeroes them
+            const float nm_now = seen ? -m_new : 0.f;
+            nm[c] = seen ? -m_new : INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm_now);
+            rs[c] = sum16(pv[c]);
+          }
+        }
+
         bf16x8 pk[NQ][2];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-          // rows with nothing visible yet keep m = -inf; exponentiate against 0
-          const float m_use = (partial && m_run[c] == -INFINITY) ? 0.f : m_run[c];
-          float pv[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if constexpr (SCORE == FLEX_SCORE_IDENTITY)
-              pv[r] = __builtin_amdgcn_exp2f(fmaf(s[c][r], c1, -m_use));
-            else
-              pv[r] = __builtin_amdgcn_exp2f(s[c][r] - m_use);
-          }
-          float rowsum = pv[0];  // fp32 sum: the LSE needs ~1e-4 relative accuracy
-#pragma unroll
-          for (int r = 1; r < 16; ++r) rowsum += pv[r];
-          l_run[c] = fmaf(l_run[c], alpha[c], rowsum);
+          l_run[c] = fmaf(l_run[c], alpha[c], rs[c]);
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             unsigned w[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              w[i] = __builtin_bit_cast(
-                  unsigned, bf16x2{(__bf16)pv[8 * hh + 2 * i], (__bf16)pv[8 * hh + 2 * i + 1]});
+              w[i] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)pv[c][8 * hh + 2 * i],
+                                                         (__bf16)pv[c][8 * hh + 2 * i + 1]});
             pk[c][hh] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
           }
         }
@@ -374,6 +521,7 @@ struct Bf16Fwd {
         // O^T += V^T P^T; the alpha rescale first (per D-half with SUB)
         constexpr int NHALF = (SUB && NE >= 2) ? 2 : 1;
         constexpr int EPH = NE / NHALF;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int half = 0; half < NHALF; ++half) {
           if (rescale) {
@@ -391,24 +539,32 @@ struct Bf16Fwd {
                 o[c][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[e][hh], pk[c][hh],
                                                                   o[c][e], 0, 0, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
-      __syncthreads();  // the next step's loads have landed; this buffer is free
-      if (last_part) {
-        kb_cur = kb_nxt;
-        kb_nxt = kb_after;
-      }
+      // the loads of steps n + 2 .. n + NSTAGE - 1 may stay in flight
+      step_barrier(NSTAGE - 2);
     };
 
+    // prologue: steps 0 .. NSTAGE - 2 in flight (clamped like the step
+    // loads), then wait for step 0
     if (nsteps > 0) {
-      kb_cur = tile_kb(0);
-      if (ntiles > 1) kb_nxt = tile_kb(1);
-      dma(buf[0], kb_cur, 0);
+#pragma unroll
+      for (int m = 0; m < NSTAGE - 1; ++m) dma(buf[m], min(m, nsteps - 1));
     }
-    __syncthreads();
-    for (int n = 0; n < nsteps; n += 2) {
+    step_barrier(NSTAGE - 2);
+    // whole rounds of NSTAGE steps, straight-line, then the remainder
+    int n = 0;
+    for (; n + NSTAGE <= nsteps; n += NSTAGE) {
       step(Int<0>(), n);
-      if (n + 1 < nsteps) step(Int<1>(), n + 1);
+      step(Int<1>(), n + 1);
+      if constexpr (NSTAGE > 2) step(Int<2 % NSTAGE>(), n + 2);
+      if constexpr (NSTAGE > 3) step(Int<3 % NSTAGE>(), n + 3);
     }
+    if (n < nsteps) step(Int<0>(), n);
+    if (n + 1 < nsteps) step(Int<1 % NSTAGE>(), n + 1);
+    if constexpr (NSTAGE > 2)
+      if (n + 2 < nsteps) step(Int<2 % NSTAGE>(), n + 2);
+    wait_vmcnt<0>();  // leave no load in flight behind the kernel
 
     // ---- epilogue: out = acc / l, lse = (m + log2 l) ln 2 ----
 #pragma unroll

@@ -214,3 +214,52 @@ def test_single_row_single_key():
     out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
     np.testing.assert_array_equal(out[0, 0, 0], v[0, 0, 0].double().numpy())
     assert math.isfinite(float(lse[0, 0, 0]))
+
+
+def _with_direction(cfg, key_col0, q_col0=1.0):
+    """The workload's inputs with q[..., 0] = q_col0 and k[..., 0] set from
+    key_col0 (a function of the key index), stored in the workload dtype."""
+    q, k, v = make_inputs(cfg)
+    dt = q.dtype
+    qf, kf = q.float().clone(), k.float().clone()
+    qf[..., 0] = q_col0
+    kf[..., 0] = key_col0(torch.arange(cfg["kv_len"], dtype=torch.float32))
+    return qf.to(dt).contiguous(), kf.to(dt).contiguous(), v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("trend", [4.0, -4.0])
+@pytest.mark.parametrize("mask", [{"kind": "causal"},
+                                  {"kind": "sliding_window", "window": 150, "window_min": 0}])
+def test_monotone_score_trend(dtype, trend, mask):
+    """Scores that rise (or fall) by about 23 log2 units per 32 keys.  Rising,
+    nearly every block raises the row's offset (the kernel's rescale path);
+    falling, later probabilities underflow to zero.  Same tolerances as the
+    other parity tests."""
+    cfg = workload("tiny_causal", B=1, H=2, q_len=333, kv_len=333, dtype=dtype, mask=mask)
+    q, k, v = _with_direction(cfg, lambda j: trend * j)
+    for od in ("fp32", "bf16"):
+        out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=getattr(torch, {"fp32": "float32", "bf16": "bfloat16"}[od]),
+                              lse=True)
+        ref_out, ref_lse = oracle_rows(cfg, q, k, v)
+        compare(out.reshape(-1, cfg["d"]), lse.reshape(-1), ref_out, ref_lse, dtype, od,
+                what="trend %g %s %s" % (trend, mask["kind"], od))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_score_spike_mid_row(dtype):
+    """One key (index 150) scores about 72 log2 units above every other key
+    of a row: rows that reach it switch their offset there, mid-row and
+    mid-tile."""
+    cfg = workload("prefix_causal", B=1, H=2, q_len=400, kv_len=400, dtype=dtype,
+                   mask={"kind": "causal"}, q_block=128, kv_block=64)
+    q, k, v = _with_direction(cfg, lambda j: torch.where(j == 150, 400.0, 0.0))
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
+    ref_out, ref_lse = oracle_rows(cfg, q, k, v)
+    compare(out.reshape(-1, cfg["d"]), lse.reshape(-1), ref_out, ref_lse, dtype, "fp32",
+            what="spike")
+    # rows past the spike return v[150] up to the tolerance
+    o = out.reshape(cfg["B"], cfg["H"], cfg["q_len"], cfg["d"])
+    vf = v.double().numpy()
+    tol = 1e-2 if dtype == "bf16" else 1e-4
+    assert np.abs(o[:, :, 150:, :] - vf[:, :, 150:151, :]).max() <= tol
