@@ -122,6 +122,41 @@ def _row_counts(mask, q_len, kv_len):
     return np.maximum(hi - lo + 1, 0)
 
 
+def _counter_mean_kib(csv_path: str, kernel_substr: str, counter: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"].startswith(counter)]
+    if not vals:
+        raise SystemExit("no %s samples for %r in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals) / len(vals)
+
+
+def write_traffic_file(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                       workload_name: str, nbytes: int = 1 << 30):
+    """HBM bytes per forward launch from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a plain
+    device copy of `nbytes` (the copy reads and writes nbytes)."""
+    copy = "copyBuffer"
+    f_scale = nbytes / (1024.0 * _counter_mean_kib(copy_fetch_csv, copy, "FETCH_SIZE"))
+    w_scale = nbytes / (1024.0 * _counter_mean_kib(copy_write_csv, copy, "WRITE_SIZE"))
+    fetch = 1024.0 * _counter_mean_kib(fetch_csv, "fwd_kernel", "FETCH_SIZE") * f_scale
+    write = 1024.0 * _counter_mean_kib(write_csv, "fwd_kernel", "WRITE_SIZE") * w_scale
+    lines = [
+        "# HBM traffic of the forward kernel, workload %s" % workload_name,
+        "# from: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "#   and the same counters over: python bench.py --copy-calibration (a 1 GiB device copy)",
+        "# counter scale factors from the copy: FETCH_SIZE x%.4f, WRITE_SIZE x%.4f" % (f_scale, w_scale),
+        "workload = %s" % workload_name,
+        "kernel_source_hash = %s" % kernel_source_hash(),
+        "fetch_bytes_per_launch = %.0f" % fetch,
+        "write_bytes_per_launch = %.0f" % write,
+        "hbm_bytes_per_launch = %.0f" % (fetch + write),
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def copy_calibration(nbytes: int, reps: int):
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
@@ -144,7 +179,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the traffic summary under profiles/ from rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
+    if args.traffic_from:
+        write_traffic_file(*args.traffic_from, workload_name=args.workload or "prefix_causal")
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
