@@ -179,6 +179,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="forward launches timed after a cache-evicting write (0: skip)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the traffic summary under profiles/ from rocprofv3 counter CSVs")
     args = ap.parse_args(argv)
@@ -237,6 +239,19 @@ def main(argv=None):
 
     ms_per_step = elapsed * 1e3 / args.steps
     fwd_ms = [a.elapsed_time(b) for a, b in events]
+
+    # Cold-cache forward time (reported beside the warm figure, not `value`):
+    # a 1 GiB write between launches evicts L2 and the 256 MB last-level cache.
+    cold_ms = []
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(args.cold_reps):
+            flush.fill_(1.0)
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            step(ev)
+            torch.cuda.synchronize()
+            cold_ms.append(ev[0].elapsed_time(ev[1]))
+        del flush
     fwd_avg_ms = float(np.mean(fwd_ms))
     pairs = visible_pairs(cfg["mask"], Lq, Lk)
     flops = 4.0 * B * H * D * pairs
@@ -268,6 +283,7 @@ def main(argv=None):
         "pct_peak": round(100.0 * value / peak, 2),
         "fwd_ms": round(fwd_avg_ms, 5),
         "fwd_ms_min": round(float(np.min(fwd_ms)), 5),
+        "fwd_ms_cold": round(float(np.median(cold_ms)), 5) if cold_ms else None,
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
