@@ -40,6 +40,27 @@
  *    order, so each row is a permutation of 0..n_kv_blocks-1.  The field
  *    names come from the block-mask tuple of the flex_attention
  *    higher-order-op call in the test hunks of the subtiling page.
+ *
+ *  - Transposed block arrays (oracle_block_mask_t).  The same tile classes,
+ *    listed per kv-block column: q_num_blocks / q_indices and
+ *    full_q_num_blocks / full_q_indices, the second half of the block-mask
+ *    tuple in those test hunks (the arrays the backward pass walks).
+ *
+ *  - Backward (oracle_attention_backward).  The flex_attention_backward call
+ *    in the same test hunks takes q, k, v, the forward output and
+ *    log-sum-exp, the output gradient and a log-sum-exp gradient, and returns
+ *    the gradients of q, k and v.  The oracle is the derivative of the
+ *    forward definition above, written out with the chain rule for every
+ *    visible pair (i, j):
+ *      p_ij = exp(s_ij - lse_i)                     (the softmax weight)
+ *      delta_i = <dout_i, out_i> - dlse_i
+ *      ds_ij = p_ij * (<dout_i, v_j> - delta_i)     (gradient of s_ij)
+ *      dq_i += scale * ds_ij * k_j,  dk_j += scale * ds_ij * q_i,
+ *      dv_j += p_ij * dout_i.
+ *    out and lse are the oracle's own fp64 forward values.  The score
+ *    modification adds a term independent of q and k, so it changes p but
+ *    not the two products.  Masked pairs and rows that see no key contribute
+ *    nothing.
  */
 #include <math.h>
 #include <stdint.h>
@@ -203,5 +224,147 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
   }
   free(s);
   free(acc);
+  return 0;
+}
+
+/* Brute-force transposed block arrays: per kv-block column, the partial and
+ * full q-blocks ascending, then every other q-block ascending.  Shapes
+ * [nKVB] and [nKVB, nQB].  Returns 0, or -1 on a bad argument. */
+int oracle_block_mask_t(int kind, int64_t window, int64_t window_min,
+                        int64_t prefix, int64_t q_len, int64_t kv_len,
+                        int64_t q_block, int64_t kv_block, int32_t* q_num_blocks,
+                        int32_t* q_indices, int32_t* full_q_num_blocks,
+                        int32_t* full_q_indices) {
+  if (kind < 0 || kind > 3 || q_len < 0 || kv_len < 0 || q_block <= 0 ||
+      kv_block <= 0)
+    return -1;
+  int64_t nq = (q_len + q_block - 1) / q_block;
+  int64_t nk = (kv_len + kv_block - 1) / kv_block;
+  int* cls = (int*)malloc(sizeof(int) * (size_t)(nq > 0 ? nq : 1));
+  if (!cls) return -1;
+  for (int64_t kb = 0; kb < nk; ++kb) {
+    for (int64_t qb = 0; qb < nq; ++qb) {
+      int64_t count = 0;
+      for (int64_t i = qb * q_block; i < (qb + 1) * q_block; ++i)
+        for (int64_t j = kb * kv_block; j < (kb + 1) * kv_block; ++j)
+          count += mask_true(kind, window, window_min, prefix, i, j, q_len,
+                             kv_len) == 1;
+      cls[qb] = count == 0 ? 0 : (count == q_block * kv_block ? 2 : 1);
+    }
+    for (int want = 1; want <= 2; ++want) {
+      int32_t* num = want == 1 ? q_num_blocks : full_q_num_blocks;
+      int32_t* idx = (want == 1 ? q_indices : full_q_indices) + kb * nq;
+      int64_t w = 0;
+      for (int64_t qb = 0; qb < nq; ++qb)
+        if (cls[qb] == want) idx[w++] = (int32_t)qb;
+      num[kb] = (int32_t)w;
+      for (int64_t qb = 0; qb < nq; ++qb)
+        if (cls[qb] != want) idx[w++] = (int32_t)qb;
+    }
+  }
+  free(cls);
+  return 0;
+}
+
+/*
+ * Backward for a list of heads.  q, dout are [B, H, q_len, d] / [.., dv],
+ * k, v are [B, H, kv_len, d] / [.., dv], all float32 holding the exact
+ * values; dlse is [B, H, q_len] or NULL (zero).  heads[t] is the flat head
+ * id b * H + h.  Writes the fp64 gradients of the listed heads into
+ * dq [B*H*q_len*d], dk [B*H*kv_len*d], dv [B*H*kv_len*dv] (the slabs of
+ * other heads are left alone).  Returns 0, or -1 on a bad argument or
+ * allocation failure.
+ */
+int oracle_attention_backward(const float* q, const float* k, const float* v,
+                              const float* dout, const float* dlse, int64_t B,
+                              int64_t H, int64_t q_len, int64_t kv_len,
+                              int64_t d, int64_t dv, int mask_kind,
+                              int64_t window, int64_t window_min, int64_t prefix,
+                              int score_kind, double bias_max, double scale,
+                              const int64_t* heads, int64_t n_heads, double* dq,
+                              double* dk, double* dvg) {
+  if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
+    return -1;
+  if (mask_kind < 0 || mask_kind > 3) return -1;
+  if (score_kind != ORACLE_SCORE_IDENTITY && score_kind != ORACLE_SCORE_REL_BIAS)
+    return -1;
+  size_t nk = (size_t)(kv_len > 0 ? kv_len : 1);
+  double* s = (double*)malloc(sizeof(double) * nk);
+  double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+  if (!s || !o) {
+    free(s);
+    free(o);
+    return -1;
+  }
+  for (int64_t t = 0; t < n_heads; ++t) {
+    int64_t bh = heads[t];
+    if (bh < 0 || bh >= B * H) {
+      free(s);
+      free(o);
+      return -1;
+    }
+    int64_t h = bh % H;
+    double slope = pow(2.0, -bias_max * (double)(h + 1) / (double)H);
+    const float* qh = q + bh * q_len * d;
+    const float* kh = k + bh * kv_len * d;
+    const float* vh = v + bh * kv_len * dv;
+    const float* doh = dout + bh * q_len * dv;
+    double* dqh = dq + bh * q_len * d;
+    double* dkh = dk + bh * kv_len * d;
+    double* dvh = dvg + bh * kv_len * dv;
+    for (int64_t x = 0; x < q_len * d; ++x) dqh[x] = 0.0;
+    for (int64_t x = 0; x < kv_len * d; ++x) dkh[x] = 0.0;
+    for (int64_t x = 0; x < kv_len * dv; ++x) dvh[x] = 0.0;
+    for (int64_t i = 0; i < q_len; ++i) {
+      /* forward for row i: scores, max, sum, output, lse */
+      double mx = -INFINITY;
+      int any = 0;
+      for (int64_t j = 0; j < kv_len; ++j) {
+        if (mask_true(mask_kind, window, window_min, prefix, i, j, q_len,
+                      kv_len) != 1) {
+          s[j] = -INFINITY;
+          continue;
+        }
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+          dot += (double)qh[i * d + c] * (double)kh[j * d + c];
+        double sj = scale * dot;
+        if (score_kind == ORACLE_SCORE_REL_BIAS) sj -= slope * (double)(i - j);
+        s[j] = sj;
+        if (sj > mx) mx = sj;
+        any = 1;
+      }
+      if (!any) continue;
+      double l = 0.0;
+      for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
+      for (int64_t j = 0; j < kv_len; ++j) {
+        if (s[j] == -INFINITY) continue;
+        double w = exp(s[j] - mx);
+        l += w;
+        for (int64_t c = 0; c < dv; ++c) o[c] += w * (double)vh[j * dv + c];
+      }
+      for (int64_t c = 0; c < dv; ++c) o[c] /= l;
+      double lse = mx + log(l);
+      /* delta_i = <dout_i, out_i> - dlse_i */
+      double delta = 0.0;
+      for (int64_t c = 0; c < dv; ++c) delta += (double)doh[i * dv + c] * o[c];
+      if (dlse) delta -= (double)dlse[bh * q_len + i];
+      for (int64_t j = 0; j < kv_len; ++j) {
+        if (s[j] == -INFINITY) continue;
+        double p = exp(s[j] - lse);
+        double dp = 0.0;
+        for (int64_t c = 0; c < dv; ++c)
+          dp += (double)doh[i * dv + c] * (double)vh[j * dv + c];
+        double ds = p * (dp - delta);
+        for (int64_t c = 0; c < d; ++c) {
+          dqh[i * d + c] += scale * ds * (double)kh[j * d + c];
+          dkh[j * d + c] += scale * ds * (double)qh[i * d + c];
+        }
+        for (int64_t c = 0; c < dv; ++c) dvh[j * dv + c] += p * (double)doh[i * dv + c];
+      }
+    }
+  }
+  free(s);
+  free(o);
   return 0;
 }

@@ -69,6 +69,13 @@ def _load():
             + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p]
         )
         lib.oracle_attention_rows.restype = ctypes.c_int
+        lib.oracle_block_mask_t.argtypes = [ctypes.c_int] + [i64] * 7 + [i32p] * 4
+        lib.oracle_block_mask_t.restype = ctypes.c_int
+        lib.oracle_attention_backward.argtypes = (
+            [f32p, f32p, f32p, f32p, f32p] + [i64] * 6 + [ctypes.c_int, i64, i64, i64]
+            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
+        )
+        lib.oracle_attention_backward.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -111,6 +118,27 @@ def block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int)
     )
     if r != 0:
         raise ValueError("oracle_block_mask rejected its arguments")
+    return tuple(arrs)
+
+
+def block_mask_t(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int):
+    """Brute-force transposed block arrays: (q_num_blocks, q_indices,
+    full_q_num_blocks, full_q_indices) as int32 numpy arrays of shapes
+    [nKVB], [nKVB, nQB]."""
+    nq = -(-q_len // q_block)
+    nk = -(-kv_len // kv_block)
+    arrs = [
+        np.zeros(nk, np.int32),
+        np.zeros((nk, nq), np.int32),
+        np.zeros(nk, np.int32),
+        np.zeros((nk, nq), np.int32),
+    ]
+    ptrs = [a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for a in arrs]
+    r = _load().oracle_block_mask_t(
+        *_mask_args(mask), q_len, kv_len, q_block, kv_block, *ptrs
+    )
+    if r != 0:
+        raise ValueError("oracle_block_mask_t rejected its arguments")
     return tuple(arrs)
 
 
@@ -171,6 +199,57 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
     if any(c != 0 for c in codes):
         raise ValueError("oracle_attention_rows rejected its arguments")
     return out, lse
+
+
+def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dlse=None,
+                       threads: int | None = None):
+    """fp64 gradients (dq, dk, dv) of every head.
+
+    q: [B, H, Lq, D], k: [B, H, Lkv, D], v: [B, H, Lkv, Dv], dout: [B, H, Lq, Dv]
+    float32 arrays (exact values); dlse: [B, H, Lq] or None.  Heads are
+    independent and are spread over host threads.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    B, H, Lq, D = q.shape
+    Lkv, Dv = k.shape[2], v.shape[3]
+    assert k.shape == (B, H, Lkv, D) and v.shape == (B, H, Lkv, Dv)
+    assert dout.shape == (B, H, Lq, Dv)
+    if dlse is not None:
+        dlse = np.ascontiguousarray(dlse, dtype=np.float32)
+        assert dlse.shape == (B, H, Lq)
+    dq = np.zeros((B, H, Lq, D), np.float64)
+    dk = np.zeros((B, H, Lkv, D), np.float64)
+    dv = np.zeros((B, H, Lkv, Dv), np.float64)
+    score_kind = SCORE_KINDS[score.get("kind", "identity")]
+    bias_max = float(score.get("bias_max", 8.0))
+    lib = _load()
+    margs = _mask_args(mask)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    ptr = lambda a: a.ctypes.data_as(f32p)
+    dlp = ptr(dlse) if dlse is not None else None
+    heads = np.arange(B * H, dtype=np.int64)
+
+    def run(t):
+        hs = heads[t:t + 1]
+        return lib.oracle_attention_backward(
+            ptr(q), ptr(k), ptr(v), ptr(dout), dlp, B, H, Lq, Lkv, D, Dv, *margs,
+            score_kind, bias_max, float(scale),
+            hs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1,
+            dq.ctypes.data_as(f64p), dk.ctypes.data_as(f64p), dv.ctypes.data_as(f64p))
+
+    nthr = threads or _cpu_threads()
+    if nthr == 1 or B * H <= 1:
+        codes = [run(t) for t in range(B * H)]
+    else:
+        with ThreadPoolExecutor(min(nthr, B * H)) as ex:
+            codes = list(ex.map(run, range(B * H)))
+    if any(c != 0 for c in codes):
+        raise ValueError("oracle_attention_backward rejected its arguments")
+    return dq, dk, dv
 
 
 def threads_used(threads: int | None = None) -> int:
