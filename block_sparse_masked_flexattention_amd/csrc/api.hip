@@ -104,6 +104,44 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
              : FLEX_E_HIP;
 }
 
+int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
+                                     int32_t kv_len, int32_t q_block,
+                                     int32_t kv_block, int32_t* q_num_blocks,
+                                     int32_t* q_indices,
+                                     int32_t* full_q_num_blocks,
+                                     int32_t* full_q_indices, void* stream) {
+  if (!mask) return FLEX_E_INVALID_ARG;
+  if (q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0 ||
+      q_block > 1024 || kv_block > 1024)
+    return FLEX_E_INVALID_ARG;
+  int32_t err = FLEX_OK;
+  if (!mask_ok(*mask, &err)) return err;
+  const int32_t nq = ceil_div(q_len, q_block), nk = ceil_div(kv_len, kv_block);
+  if ((int64_t)nq * nk > INT32_MAX) return FLEX_E_INVALID_ARG;
+  if (nk > 0 && (!q_num_blocks || !full_q_num_blocks)) return FLEX_E_INVALID_ARG;
+  if (nq > 0 && nk > 0 && (!q_indices || !full_q_indices)) return FLEX_E_INVALID_ARG;
+  if (nk == 0) return FLEX_OK;
+
+  MaskBuildParams p;
+  p.kind = mask->kind;
+  p.window = mask->window;
+  p.window_min = mask->window_min;
+  p.prefix = mask->prefix;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.q_block = q_block;
+  p.kv_block = kv_block;
+  p.n_qb = nq;
+  p.n_kb = nk;
+  p.kv_num = q_num_blocks;
+  p.kv_idx = q_indices;
+  p.fkv_num = full_q_num_blocks;
+  p.fkv_idx = full_q_indices;
+  return launch_block_mask_t(p, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FLEX_OK
+             : FLEX_E_HIP;
+}
+
 int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
                       int32_t kv_len, int32_t head_dim,
@@ -175,6 +213,112 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   const bool sub = opt != nullptr && opt->use_subtiling != 0;
   return launch_fwd(p, in_dtype, head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
                     score_kind, sub, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? FLEX_OK
+             : FLEX_E_HIP;
+}
+
+
+int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
+                                       int64_t* n_floats) {
+  if (!n_floats || B < 0 || H < 0 || q_len < 0) return FLEX_E_INVALID_ARG;
+  *n_floats = 2 * (int64_t)B * H * q_len;
+  return FLEX_OK;
+}
+
+int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, const float* dlse,
+                      int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
+                      int32_t kv_len, int32_t head_dim, const flex_block_mask* bm,
+                      const flex_block_mask_t* bmt, const flex_score_desc* score,
+                      float scale, void* dq, void* dk, void* dv, int32_t grad_dtype,
+                      float* workspace, void* stream) {
+  if (!bm || !bmt) return FLEX_E_INVALID_ARG;
+  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0)
+    return FLEX_E_INVALID_ARG;
+  if (in_dtype != FLEX_DTYPE_BF16 && in_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
+  if (grad_dtype != FLEX_DTYPE_BF16 && grad_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
+  if (!isfinite(scale) || scale == 0.0f) return FLEX_E_UNSUPPORTED;
+  if (bm->q_len != q_len || bm->kv_len != kv_len) return FLEX_E_INVALID_ARG;
+  if (bm->q_block <= 0 || bm->kv_block <= 0) return FLEX_E_INVALID_ARG;
+  if (bm->n_q_blocks != ceil_div(q_len, bm->q_block) ||
+      bm->n_kv_blocks != ceil_div(kv_len, bm->kv_block))
+    return FLEX_E_INVALID_ARG;
+  if (bmt->q_block != bm->q_block || bmt->kv_block != bm->kv_block ||
+      bmt->n_q_blocks != bm->n_q_blocks || bmt->n_kv_blocks != bm->n_kv_blocks)
+    return FLEX_E_INVALID_ARG;
+  int32_t err = FLEX_OK;
+  if (!mask_ok(bm->mask, &err)) return err;
+  int32_t score_kind = FLEX_SCORE_IDENTITY;
+  float bias_max = 0.f;
+  if (score) {
+    score_kind = score->kind;
+    if (score_kind != FLEX_SCORE_IDENTITY && score_kind != FLEX_SCORE_REL_BIAS)
+      return FLEX_E_UNSUPPORTED;
+    if (score_kind == FLEX_SCORE_REL_BIAS) {
+      if (score->num_heads != H || !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      bias_max = score->bias_max;
+    }
+  }
+  if (!bwd_supported(in_dtype, head_dim, bm->q_block, bm->kv_block))
+    return FLEX_E_UNSUPPORTED;
+
+  const int64_t rows = (int64_t)B * H * q_len;
+  const int64_t krows = (int64_t)B * H * kv_len;
+  if ((int64_t)B * H * bm->n_q_blocks > INT32_MAX || (int64_t)B * H * bm->n_kv_blocks > INT32_MAX ||
+      rows * head_dim > ((int64_t)1 << 40) || krows * head_dim > ((int64_t)1 << 40))
+    return FLEX_E_INVALID_ARG;
+  if (rows == 0 && krows == 0) return FLEX_OK;  // nothing to write
+  if (rows > 0 && (!q || !out || !dout || !lse || !dq || !workspace)) return FLEX_E_INVALID_ARG;
+  if (krows > 0 && (!k || !v || !dk || !dv)) return FLEX_E_INVALID_ARG;
+  if (bm->n_q_blocks > 0 && (!bm->kv_num_blocks || !bm->full_kv_num_blocks))
+    return FLEX_E_INVALID_ARG;
+  if (bm->n_q_blocks > 0 && bm->n_kv_blocks > 0 && (!bm->kv_indices || !bm->full_kv_indices))
+    return FLEX_E_INVALID_ARG;
+  if (bmt->n_kv_blocks > 0 && (!bmt->q_num_blocks || !bmt->full_q_num_blocks))
+    return FLEX_E_INVALID_ARG;
+  if (bmt->n_q_blocks > 0 && bmt->n_kv_blocks > 0 && (!bmt->q_indices || !bmt->full_q_indices))
+    return FLEX_E_INVALID_ARG;
+  const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out |
+                          (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+  if ((align & 15u) || ((uintptr_t)workspace & 3u)) return FLEX_E_INVALID_ARG;
+
+  BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.dlse = dlse;
+  p.ws = workspace;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.kv_num = bm->kv_num_blocks;
+  p.kv_idx = bm->kv_indices;
+  p.fkv_num = bm->full_kv_num_blocks;
+  p.fkv_idx = bm->full_kv_indices;
+  p.q_num = bmt->q_num_blocks;
+  p.q_idx = bmt->q_indices;
+  p.fq_num = bmt->full_q_num_blocks;
+  p.fq_idx = bmt->full_q_indices;
+  p.B = B;
+  p.H = H;
+  p.q_len = q_len;
+  p.kv_len = kv_len;
+  p.n_qb = bm->n_q_blocks;
+  p.n_kb = bm->n_kv_blocks;
+  p.window = bm->mask.window;
+  p.window_min = bm->mask.window_min;
+  p.prefix = bm->mask.prefix;
+  p.c1 = fabsf(scale) * 1.44269504088896340736f;
+  p.scale = scale;
+  p.inv_abs_scale = 1.0f / fabsf(scale);
+  p.neg = scale < 0.f ? 1 : 0;
+  p.bias_max = bias_max;
+  p.grad_bf16 = grad_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
+  return launch_bwd(p, head_dim, bm->q_block, bm->kv_block, bm->mask.kind, score_kind,
+                    static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
 }

@@ -173,7 +173,67 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildPar
   }
 }
 
+// Transposed arrays (q_num_blocks / q_indices / full_q_num_blocks /
+// full_q_indices, the second half of the same block-mask tuple): one
+// work-group per kv-block column, one thread per (q-block, kv-block) tile.
+// The thread classifies its tile from the q-block's row intervals exactly as
+// above (full: every row in range and its interval covering the in-range
+// tile; partial: some row's interval meeting the tile's columns), then the
+// same two-pass prefix count orders the column: selected q-blocks ascending,
+// then the others ascending.  The kv_num / kv_idx / fkv_num / fkv_idx fields
+// of the parameters carry the four transposed arrays here.
+__global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildParams p) {
+  __shared__ int scratch[kWaves];
+  const int kb = blockIdx.x;
+  const int nq = p.n_qb;
+  const size_t col = (size_t)kb * nq;
+  const int c0 = kb * p.kv_block;
+  const int c_end = c0 + p.kv_block - 1;
+  const int c_last = min(c_end, p.kv_len - 1);  // c0 <= kv_len - 1 since kb < n_kb
+  int n_part = 0, n_full = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    int seen_part = 0, seen_full = 0;
+    for (int q00 = 0; q00 < nq; q00 += kThreads) {
+      const int qb = q00 + (int)threadIdx.x;
+      int c = 0;  // 0 empty, 1 partial, 2 full
+      if (qb < nq) {
+        const int r0 = qb * p.q_block;
+        const int r1 = min(r0 + p.q_block, p.q_len);
+        bool all = r0 + p.q_block <= p.q_len && c_end < p.kv_len, any = false;
+        for (int i = r0; i < r1; ++i) {
+          const RowInterval iv = visible_keys(p, i);
+          all = all && iv.lo <= c0 && iv.hi >= c_end;
+          any = any || (iv.lo <= iv.hi && iv.lo <= c_last && iv.hi >= c0);
+        }
+        c = all ? 2 : (any ? 1 : 0);
+      }
+      int tp, tf;
+      const int bp = seen_part + block_prefix(c == 1, scratch, &tp);
+      const int bf = seen_full + block_prefix(c == 2, scratch, &tf);
+      if (pass == 1 && qb < nq) {
+        p.kv_idx[col + (c == 1 ? bp : n_part + (qb - bp))] = qb;
+        p.fkv_idx[col + (c == 2 ? bf : n_full + (qb - bf))] = qb;
+      }
+      seen_part += tp;
+      seen_full += tf;
+    }
+    n_part = seen_part;
+    n_full = seen_full;
+  }
+  if (threadIdx.x == 0) {
+    p.kv_num[kb] = n_part;
+    p.fkv_num[kb] = n_full;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream) {
+  if (p.n_kb == 0) return hipSuccess;
+  hipLaunchKernelGGL(build_block_mask_t_kernel, dim3(p.n_kb), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_mask(const MaskBuildParams& p, hipStream_t stream) {
   if (p.n_qb == 0) return hipSuccess;

@@ -1,0 +1,705 @@
+// bwd_bf16.hpp -- the backward pass (gradients of q, k and v) for bf16
+// inputs on gfx950.
+//
+// What it computes is the derivative of the forward: the flex_attention
+// backward higher-order op of "[Inductor][Flex Attention] Add Subtiling
+// Option for Alpha Scaling" (test hunks) takes q, k, v, the forward output
+// and log-sum-exp, the output gradient and a log-sum-exp gradient, and the
+// block mask with its transposed q_num_blocks / q_indices / full_q_* arrays,
+// and returns dq, dk and dv.  For every visible pair (i, j):
+//   p_ij  = exp(s_ij - lse_i)
+//   delta_i = <dout_i, out_i> - dlse_i
+//   ds_ij = p_ij (<dout_i, v_j> - delta_i)
+//   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+//   dv_j = sum_i p_ij dout_i.
+// Three kernels:
+//  * bwd_pre_kernel: per query row, -delta_i and a_i = -lse_i / |scale|
+//    (the log-sum-exp in units of the raw score; -inf for a row that sees no
+//    key), into the caller's workspace.
+//  * Bf16BwdDq: one work-group per (batch, head, q-block), one wave per 32
+//    query rows, walking the forward's tile list like the forward.  S^T and
+//    dP^T = V dout^T are taken with K and V as the A operands and q, dout in
+//    registers as B operands (lane = query row), p = 2^(c1 s + c1 a) needs no
+//    row reduction, and dq^T += K^T ds^T reads K^T with the transposing LDS
+//    read the forward uses for V^T.
+//  * Bf16BwdDkv: one work-group per (batch, head, kv-block), one wave per 32
+//    keys with that wave's K and V rows resident in registers as B operands
+//    (lane = key), walking the transposed tile list in steps of 32 query
+//    rows.  The S and dP accumulators start at a_i and -delta_i (read from
+//    LDS straight into them), so p = 2^(c1 s) and ds = p dP; then
+//    dv^T += dout^T p and dk^T += q^T ds read dout^T and q^T transposed.
+// K, V, q and dout tiles sit in LDS in the forward's V layout (rows in
+// order, 8-byte units XOR-swizzled by an even amount, so 16-byte pieces stay
+// whole for the row reads); a row read for an A operand takes row
+// swap23(lane) so that accumulator registers 8h..8h+7 hold eight
+// consecutive keys (queries), ready to be the next product's B operand.
+#pragma once
+#include "fwd_common.hpp"
+
+namespace flexattn {
+namespace bwd {
+
+using fwd::bf16x2;
+using fwd::bf16x4;
+using fwd::bf16x8;
+using fwd::f32x16;
+using fwd::f32x4;
+using fwd::u32x4;
+using fwd::kLog2e;
+using fwd::ld_global16;
+using fwd::swap23;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_t;
+
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+#define FLEXATTN_LDS(T, ptr) (*(__attribute__((address_space(3))) T*)(ptr))
+
+// V-layout swizzle of the forward: row r, 8-byte unit u at unit u ^ vswz(r)
+template <int D>
+__device__ inline int vswz(int r) {
+  return D == 64 ? ((4 * (r & 1)) ^ (8 * ((r >> 1) & 1))) : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)));
+}
+
+// Queries that see key kk, as one interval [lo, hi] (empty when lo > hi),
+// clipped to the query range: the transpose of row_interval.
+template <int MASK>
+__device__ inline void col_interval(const BwdParams& p, int kk, int& lo, int& hi) {
+  lo = 0;
+  hi = p.q_len - 1;
+  if (kk >= p.kv_len) {
+    lo = 1;
+    hi = 0;
+    return;
+  }
+  if constexpr (MASK == FLEX_MASK_CAUSAL) {
+    lo = kk;
+  } else if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) {
+    // window_min <= q - kk <= window, in 64 bits
+    lo = (int)max(0LL, (long long)kk + p.window_min);
+    hi = (int)min((long long)hi, (long long)kk + p.window);
+  } else if constexpr (MASK == FLEX_MASK_PREFIX_CAUSAL) {
+    // (q <= P and kk <= P) or q >= kk: every q when kk <= P
+    lo = kk <= p.prefix ? 0 : kk;
+  }
+}
+
+__device__ inline void s_barrier_full() {
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Store one row of an accumulator transposed like the forward's O^T:
+// register r of column block e holds column 32e + 8(r/4) + 4g + r%4.
+template <int NE>
+__device__ inline void write_row_t(void* base, bool bf16, size_t row, int D, int g,
+                                   const f32x16 (&a)[NE], float f) {
+  char* og = static_cast<char*>(base) + row * (size_t)D * (bf16 ? 2 : 4);
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = 32 * e + 8 * q + 4 * g;
+      const float v0 = a[e][4 * q] * f, v1 = a[e][4 * q + 1] * f;
+      const float v2 = a[e][4 * q + 2] * f, v3 = a[e][4 * q + 3] * f;
+      if (bf16) {
+        *reinterpret_cast<bf16x4*>(og + d * 2) =
+            bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+      } else {
+        *reinterpret_cast<f32x4*>(og + d * 4) = f32x4{v0, v1, v2, v3};
+      }
+    }
+}
+
+// bf16 B operands from 16 fp32 values: register 8h + 2i, 8h + 2i + 1 -> word i of pk[h]
+__device__ inline void pack16(const float (&x)[16], bf16x8 (&pk)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    unsigned w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)x[8 * h + 2 * i], (__bf16)x[8 * h + 2 * i + 1]});
+    pk[h] = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per query row: ws[row] = -delta, ws[rows + row] = a.  D / 8 lanes per row,
+// each reading 8 elements of out and dout.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  const long long rows = (long long)p.B * p.H * p.q_len;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / LPR;
+  const int part = (int)(t % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = ld_global16(static_cast<const char*>(p.out) + (row * D + part * 8) * 2);
+    const u32x4 d = ld_global16(static_cast<const char*>(p.dout) + (row * D + part * 8) * 2);
+    const bf16x8 ob = __builtin_bit_cast(bf16x8, o), db = __builtin_bit_cast(bf16x8, d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)ob[i], (float)db[i], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    const float delta = acc - (p.dlse != nullptr ? p.dlse[row] : 0.f);
+    const float lse = p.lse[row];
+    p.ws[row] = -delta;
+    p.ws[rows + row] = lse == -INFINITY ? -INFINITY : -lse * p.inv_abs_scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq
+// ---------------------------------------------------------------------------
+template <int D, int QB, int KB, int MASK, int SCORE>
+struct Bf16BwdDq {
+  static constexpr int NW = QB / 32;
+  static constexpr int NT = 64 * NW;
+  static constexpr int KS = 64;             // keys per step
+  static constexpr int SPT = KB / KS;
+  static constexpr int NE = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int STAGE = KS * ROWB;   // bytes of K (or V) per step
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NDMA = KS * CPR / (64 * NW);
+  static constexpr int WAVES_PER_SIMD = 2;
+  static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
+
+  __device__ static void run(const BwdParams& p) {
+    __shared__ __attribute__((aligned(16))) char sb0[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char sb1[2 * STAGE];
+    lds_t* const buf[2] = {(lds_t*)sb0, (lds_t*)sb1};
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, g = lane >> 5;
+
+    int bh, qb;
+    fwd::wg_to_tile(p.n_qb, bh, qb);
+    const int h = bh % p.H;
+    const int q0 = qb * QB;
+    const bool q_ragged = q0 + QB > p.q_len;
+    const long long rows = (long long)p.B * p.H * p.q_len;
+    const size_t head_q = (size_t)bh * p.q_len;
+    const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
+    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWB;
+    const char* kg = static_cast<const char*>(p.k) + (size_t)bh * p.kv_len * ROWB;
+    const char* vg = static_cast<const char*>(p.v) + (size_t)bh * p.kv_len * ROWB;
+
+    // A-operand row reads: row swap23(lq), 16-byte piece 2t + g in V layout
+    const int ra = swap23(lq);
+    int kra[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      kra[t] = ra * ROWB + (((2 * t + g) ^ (vswz<D>(ra) >> 1)) << 4);
+    // transposing reads (the forward's V^T fragment offsets)
+    int tro[NE];
+    {
+      const int j = lane & 15, u = (lane >> 4) & 1;
+      const int r0 = 8 * g + (j >> 2);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) tro[e] = r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz<D>(r0)) << 3);
+    }
+
+    // q and dout fragments (B operands), one query row per lane
+    const int qi = q0 + wave * 32 + lq;
+    const bool ok = qi < p.q_len;
+    u32x4 qf[D / 16], dof[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ok ? ld_global16(qg + (size_t)qi * ROWB + (2 * t + g) * 16) : u32x4{0, 0, 0, 0};
+      dof[t] = ok ? ld_global16(dog + (size_t)qi * ROWB + (2 * t + g) * 16) : u32x4{0, 0, 0, 0};
+      if (p.neg) qf[t] ^= 0x80008000u;
+    }
+    const long long row = (long long)head_q + min(qi, max(p.q_len - 1, 0));
+    const float ndelta = ok ? p.ws[row] : 0.f;
+    const float nm = ok ? p.c1 * p.ws[rows + row] : -INFINITY;  // c1 a (-inf: no key)
+    int lo, hi;
+    fwd::row_interval<MASK>(p, qi, lo, hi);
+    const float c1 = p.c1;
+    float bias_u = 0.f, bias_u16 = 0.f;
+    if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * fwd::kLn2);
+      bias_u16 = 16.0f * bias_u;
+    }
+
+    // tile list
+    const int nk = p.n_kb;
+    const int np = min(max(p.kv_num[qb], 0), nk);
+    const int nf = min(max(p.fkv_num[qb], 0), nk);
+    const int ntiles = np + nf;
+    const int nsteps = ntiles * SPT;
+    const int32_t* prow = p.kv_idx + (size_t)qb * nk;
+    const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
+    auto load_window = [&](int base) {
+      const int t = min(base + lane, ntiles - 1);
+      int v = 0;
+      if (t >= 0) v = t < np ? prow[t] : frow[t - np];
+      return v;
+    };
+    int win_base = 0;
+    int win = load_window(0);
+    int win_nx = ntiles > 64 ? load_window(64) : 0;
+    auto tile_kb = [&](int t) {
+      const int i = t - win_base;
+      const int v = i < 64 ? __builtin_amdgcn_readlane(win, i) : __builtin_amdgcn_readlane(win_nx, i - 64);
+      return min(max(v, 0), nk - 1);
+    };
+
+    // K and V of step m into a stage buffer, both in V layout
+    auto dma = [&](lds_t* dst, int m) {
+      const int kb = tile_kb(m / SPT);
+      const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
+      const int rows_left = min(KS, p.kv_len - kv0);
+      const char* kt = kg + (size_t)kv0 * ROWB;
+      const char* vt = vg + (size_t)kv0 * ROWB;
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int sl = (wave * NDMA + j) * 64 + lane;
+        const int r = sl / CPR, q = sl % CPR;
+        const int rr = min(r, rows_left - 1);
+        const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+        __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMA + j) * 1024), 16, 0, 0);
+      }
+    };
+
+    f32x16 acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
+
+    auto block = [&](const lds_t* cur, int b, int kvl, bool partial) {
+      // S^T = K q^T (accumulator starts at the bias for REL_BIAS)
+      f32x16 s;
+      if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+        float a0 = bias_u * (float)(qi - kvl);
+        asm volatile("" : "+v"(a0));
+        float x = a0, y = a0 - bias_u16;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          s[r] = x;
+          s[8 + r] = y;
+          x -= bias_u;
+          y -= bias_u;
+        }
+      } else {
+        s = f32x16{};
+      }
+      f32x16 dp = f32x16{};
+      bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        kf[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + kra[t] + 32 * b * ROWB));
+        vf[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + STAGE + kra[t] + 32 * b * ROWB));
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], __builtin_bit_cast(bf16x8, qf[t]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], __builtin_bit_cast(bf16x8, dof[t]), dp, 0, 0, 0);
+      }
+      // K^T fragments for dq^T += K^T ds^T
+      bf16x8 ktf[NE][2];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const lds_t* vp = cur + tro[e] + (32 * b + 16 * hh) * ROWB;
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)vp);
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp + 4 * ROWB));
+          ktf[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      // p = 2^(c1 s + c1 a), masked on partial tiles; ds = p (dP - delta)
+      float ds[16];
+      const int lim_hi = hi - kvl, lim_lo = lo - kvl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(fmaf(s[r], c1, nm));
+        if (partial) {
+          const int off = 16 * (r >> 3) + (r & 7);
+          bool vis = off <= lim_hi;
+          if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) vis = vis && off >= lim_lo;
+          pr = vis ? pr : 0.f;
+        }
+        ds[r] = pr * (dp[r] + ndelta);
+      }
+      bf16x8 pk[2];
+      pack16(ds, pk);
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[e][hh], pk[hh], acc[e], 0, 0, 0);
+    };
+
+    auto step = [&](auto buf_tag, int n) {
+      constexpr int B = decltype(buf_tag)::value;
+      const lds_t* cur = buf[B];
+      const int t = n / SPT, part = n % SPT;
+      if (t >= win_base + 64) {
+        win_base += 64;
+        win = win_nx;
+        if (win_base + 64 < ntiles) win_nx = load_window(win_base + 64);
+      }
+      const int kb = tile_kb(t);
+      const int kv0 = kb * KB + part * KS;
+      const bool partial = t < np || q_ragged || kb * KB + KB > p.kv_len;
+      if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
+#pragma unroll
+      for (int b = 0; b < KS / 32; ++b) {
+        if (partial) {
+          const int b0 = kv0 + 32 * b;
+          const bool any = lo <= b0 + 31 && hi >= b0 && lo <= hi;
+          if (!__any(any)) continue;
+        }
+        block(cur, b, kv0 + 32 * b + 8 * g, partial);
+      }
+      s_barrier_full();
+    };
+
+    if (nsteps > 0) dma(buf[0], 0);
+    s_barrier_full();
+    int n = 0;
+    for (; n + 2 <= nsteps; n += 2) {
+      step(Int<0>(), n);
+      step(Int<1>(), n + 1);
+    }
+    if (n < nsteps) step(Int<0>(), n);
+
+    if (ok) write_row_t<NE>(p.dq, p.grad_bf16 != 0, head_q + qi, D, g, acc, p.scale);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// dk, dv
+// ---------------------------------------------------------------------------
+template <int D, int QB, int KB, int MASK, int SCORE>
+struct Bf16BwdDkv {
+  static constexpr int NW = KB / 32;        // one wave per 32 keys
+  static constexpr int NT = 64 * NW;
+  static constexpr int QS = 32;             // query rows per step
+  static constexpr int SPQ = QB / QS;       // steps per listed q-block
+  static constexpr int NE = D / 32;
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILE = QS * ROWB;    // bytes of q (or dout) per step
+  static constexpr int ARR = TILE * 2;      // offset of the per-row arrays
+  static constexpr int STAGEB = ARR + 2 * QS * 4;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int NDMA = QS * CPR / (64 * NW);
+  static constexpr int WAVES_PER_SIMD = 2;
+  static_assert(NDMA * 64 * NW == QS * CPR, "step split");
+
+  __device__ static void run(const BwdParams& p) {
+    __shared__ __attribute__((aligned(16))) char sb0[STAGEB];
+    __shared__ __attribute__((aligned(16))) char sb1[STAGEB];
+    lds_t* const buf[2] = {(lds_t*)sb0, (lds_t*)sb1};
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, g = lane >> 5;
+
+    // (head, kv-block): the forward's order with the kv-block reversed, so the
+    // kv-blocks the most q-blocks see (the first ones, under causal masks)
+    // start first
+    int bh, kbr;
+    fwd::wg_to_tile(p.n_kb, bh, kbr);
+    const int kb = p.n_kb - 1 - kbr;
+    const int h = bh % p.H;
+    const long long rows = (long long)p.B * p.H * p.q_len;
+    const size_t head_q = (size_t)bh * p.q_len;
+    const size_t head_kv = (size_t)bh * p.kv_len;
+    const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
+    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWB;
+    const bool kv_ragged = kb * KB + KB > p.kv_len;
+
+    // this lane's key, its K and V rows (B operands), its visible queries
+    const int kk = kb * KB + wave * 32 + lq;
+    const bool kok = kk < p.kv_len;
+    const int kcl = min(kk, p.kv_len - 1);
+    u32x4 kf[D / 16], vf[D / 16];
+    {
+      const char* kr = static_cast<const char*>(p.k) + (head_kv + kcl) * ROWB;
+      const char* vr = static_cast<const char*>(p.v) + (head_kv + kcl) * ROWB;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        kf[t] = ld_global16(kr + (2 * t + g) * 16);
+        vf[t] = ld_global16(vr + (2 * t + g) * 16);
+        if (p.neg) kf[t] ^= 0x80008000u;
+      }
+    }
+    int qlo, qhi;
+    col_interval<MASK>(p, kk, qlo, qhi);
+    const float c1 = p.c1;
+    float bias_u = 0.f, bias_u16 = 0.f;
+    if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * fwd::kLn2);
+      bias_u16 = 16.0f * bias_u;
+    }
+
+    // A-operand row reads of the q / dout tiles, and transposing reads
+    const int ra = swap23(lq);
+    int qra[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qra[t] = ra * ROWB + (((2 * t + g) ^ (vswz<D>(ra) >> 1)) << 4);
+    int tro[NE];
+    {
+      const int j = lane & 15, u = (lane >> 4) & 1;
+      const int r0 = 8 * g + (j >> 2);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) tro[e] = r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz<D>(r0)) << 3);
+    }
+
+    // transposed tile list of this kv-block
+    const int nq = p.n_qb;
+    const int np = min(max(p.q_num[kb], 0), nq);
+    const int nf = min(max(p.fq_num[kb], 0), nq);
+    const int ntiles = np + nf;
+    const int nsteps = ntiles * SPQ;
+    const int32_t* prow = p.q_idx + (size_t)kb * nq;
+    const int32_t* frow = p.fq_idx + (size_t)kb * nq;
+    auto load_window = [&](int base) {
+      const int t = min(base + lane, ntiles - 1);
+      int v = 0;
+      if (t >= 0) v = t < np ? prow[t] : frow[t - np];
+      return v;
+    };
+    int win_base = 0;
+    int win = load_window(0);
+    int win_nx = ntiles > 64 ? load_window(64) : 0;
+    auto tile_qb = [&](int t) {
+      const int i = t - win_base;
+      const int v = i < 64 ? __builtin_amdgcn_readlane(win, i) : __builtin_amdgcn_readlane(win_nx, i - 64);
+      return min(max(v, 0), nq - 1);
+    };
+
+    // q and dout rows of step m (32 query rows, clamped to the last row) in
+    // V layout, then -delta and a of those rows (wave 0, one dword per lane)
+    auto dma = [&](lds_t* dst, int m) {
+      const int qbm = tile_qb(m / SPQ);
+      const int r00 = min(qbm * QB + (m % SPQ) * QS, p.q_len - 1);
+      const int rows_left = min(QS, p.q_len - r00);
+      const char* qt = qg + (size_t)r00 * ROWB;
+      const char* dt = dog + (size_t)r00 * ROWB;
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int sl = (wave * NDMA + j) * 64 + lane;
+        const int r = sl / CPR, q = sl % CPR;
+        const int rr = min(r, rows_left - 1);
+        const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+        __builtin_amdgcn_global_load_lds(qt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dt + off, (__attribute__((address_space(3))) void*)(dst + TILE + (wave * NDMA + j) * 1024), 16, 0, 0);
+      }
+      if (wave == 0) {
+        const int r = min(lq, rows_left - 1);
+        const float* src = p.ws + (g == 0 ? 0 : rows) + (long long)head_q + r00 + r;
+        // lanes 0..31: -delta, lanes 32..63: a
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + ARR), 4, 0, 0);
+      }
+    };
+
+    f32x16 dk[NE], dv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      dk[e] = f32x16{};
+      dv[e] = f32x16{};
+    }
+
+    // one step: 32 query rows q00.. against this wave's 32 keys
+    auto block = [&](const lds_t* cur, int q00, bool partial) {
+      // S = q K^T from a (the accumulator's start), + the bias for REL_BIAS;
+      // register 8h + j holds query q00 + 16h + 8g + j
+      f32x16 s, dp;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 a0 = FLEXATTN_LDS(f32x4, cur + ARR + 128 + (16 * hh + 8 * g) * 4);
+        const f32x4 a1 = FLEXATTN_LDS(f32x4, cur + ARR + 128 + (16 * hh + 8 * g + 4) * 4);
+        const f32x4 d0 = FLEXATTN_LDS(f32x4, cur + ARR + (16 * hh + 8 * g) * 4);
+        const f32x4 d1 = FLEXATTN_LDS(f32x4, cur + ARR + (16 * hh + 8 * g + 4) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[8 * hh + i] = a0[i];
+          s[8 * hh + 4 + i] = a1[i];
+          dp[8 * hh + i] = d0[i];
+          dp[8 * hh + 4 + i] = d1[i];
+        }
+      }
+      if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
+        float b0 = bias_u * (float)(q00 + 8 * g - kk);
+        asm volatile("" : "+v"(b0));
+        float x = b0, y = b0 + bias_u16;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          s[r] += x;
+          s[8 + r] += y;
+          x += bias_u;
+          y += bias_u;
+        }
+      }
+      bf16x8 qa[D / 16], da[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        qa[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + qra[t]));
+        da[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + TILE + qra[t]));
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, kf[t]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], __builtin_bit_cast(bf16x8, vf[t]), dp, 0, 0, 0);
+      }
+      // transposed fragments of dout and q for the two accumulations
+      bf16x8 dot[NE][2], qt[NE][2];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const lds_t* dp0 = cur + TILE + tro[e] + 16 * hh * ROWB;
+          const lds_t* qp0 = cur + tro[e] + 16 * hh * ROWB;
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)dp0);
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(dp0 + 4 * ROWB));
+          const i16x4 q0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)qp0);
+          const i16x4 q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(qp0 + 4 * ROWB));
+          dot[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
+          qt[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      // p = 2^(c1 s), masked on partial tiles; ds = p dP
+      float pv[16], ds[16];
+      const int lim_lo = qlo - q00 - 8 * g, lim_hi = qhi - q00 - 8 * g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(s[r] * c1);
+        if (partial) {
+          const int off = 16 * (r >> 3) + (r & 7);
+          pr = (off >= lim_lo && off <= lim_hi) ? pr : 0.f;
+        }
+        pv[r] = pr;
+        ds[r] = pr * dp[r];
+      }
+      bf16x8 pp[2], pd[2];
+      pack16(pv, pp);
+      pack16(ds, pd);
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot[e][hh], pp[hh], dv[e], 0, 0, 0);
+          dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[e][hh], pd[hh], dk[e], 0, 0, 0);
+        }
+    };
+
+    auto step = [&](auto buf_tag, int n) {
+      constexpr int B = decltype(buf_tag)::value;
+      const lds_t* cur = buf[B];
+      const int t = n / SPQ, part = n % SPQ;
+      if (t >= win_base + 64) {
+        win_base += 64;
+        win = win_nx;
+        if (win_base + 64 < ntiles) win_nx = load_window(win_base + 64);
+      }
+      const int qbt = tile_qb(t);
+      const int q00 = qbt * QB + part * QS;
+      // a listed-full tile at a ragged edge is still handled as partial
+      const bool partial = t < np || kv_ragged || qbt * QB + QB > p.q_len;
+      if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
+      bool run_it = true;
+      if (partial) {
+        const bool any = qlo <= q00 + QS - 1 && qhi >= q00 && qlo <= qhi;
+        run_it = __any(any);
+      }
+      if (run_it) block(cur, q00, partial);
+      s_barrier_full();
+    };
+
+    if (nsteps > 0) dma(buf[0], 0);
+    s_barrier_full();
+    int n = 0;
+    for (; n + 2 <= nsteps; n += 2) {
+      step(Int<0>(), n);
+      step(Int<1>(), n + 1);
+    }
+    if (n < nsteps) step(Int<0>(), n);
+
+    if (kok) {
+      write_row_t<NE>(p.dk, p.grad_bf16 != 0, head_kv + kk, D, g, dk, p.scale);
+      write_row_t<NE>(p.dv, p.grad_bf16 != 0, head_kv + kk, D, g, dv, 1.0f);
+    }
+  }
+};
+
+#undef FLEXATTN_LDS
+
+template <int D, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDq<D, QB, KB, MASK, SCORE>::NT),
+                          amdgpu_waves_per_eu(Bf16BwdDq<D, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
+void bwd_dq_kernel(BwdParams p) {
+  Bf16BwdDq<D, QB, KB, MASK, SCORE>::run(p);
+}
+
+template <int D, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDkv<D, QB, KB, MASK, SCORE>::NT),
+                          amdgpu_waves_per_eu(Bf16BwdDkv<D, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
+void bwd_dkv_kernel(BwdParams p) {
+  Bf16BwdDkv<D, QB, KB, MASK, SCORE>::run(p);
+}
+
+template <int D, int QB, int KB, int MASK, int SCORE>
+hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
+  const long long rows = (long long)p.B * p.H * p.q_len;
+  if (rows > 0) {
+    const long long threads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long nq = (long long)p.B * p.H * p.n_qb;
+  if (nq > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
+                       dim3(Bf16BwdDq<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long nkv = (long long)p.B * p.H * p.n_kb;
+  if (nkv > 0) {
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nkv),
+                       dim3(Bf16BwdDkv<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <int D, int QB, int KB, int MASK>
+hipError_t bwd_pick_score(const BwdParams& p, int score, hipStream_t s) {
+  if (score == FLEX_SCORE_REL_BIAS) return launch_bwd_one<D, QB, KB, MASK, FLEX_SCORE_REL_BIAS>(p, s);
+  return launch_bwd_one<D, QB, KB, MASK, FLEX_SCORE_IDENTITY>(p, s);
+}
+
+template <int D, int QB, int KB>
+hipError_t bwd_pick_mask(const BwdParams& p, int mask, int score, hipStream_t s) {
+  switch (mask) {
+    case FLEX_MASK_NOOP:
+      return bwd_pick_score<D, QB, KB, FLEX_MASK_NOOP>(p, score, s);
+    case FLEX_MASK_CAUSAL:
+      return bwd_pick_score<D, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
+    case FLEX_MASK_SLIDING_WINDOW:
+      return bwd_pick_score<D, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
+    default:
+      return bwd_pick_score<D, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
+  }
+}
+
+}  // namespace bwd
+}  // namespace flexattn
+
+#define FLEXATTN_BWD_UNIT(NAME, D, QB, KB)                                         \
+  namespace flexattn {                                                           \
+  hipError_t NAME(const BwdParams& p, int mask, int score, hipStream_t s) {      \
+    return bwd::bwd_pick_mask<D, QB, KB>(p, mask, score, s);                     \
+  }                                                                              \
+  }

@@ -72,8 +72,8 @@ __device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
 
 // Keys visible from query row qi, as one interval [lo, hi] (empty when
 // lo > hi), already clipped to the key range.
-template <int MASK>
-__device__ inline void row_interval(const FwdParams& p, int qi, int& lo, int& hi) {
+template <int MASK, typename P>
+__device__ inline void row_interval(const P& p, int qi, int& lo, int& hi) {
   lo = 0;
   hi = p.kv_len - 1;
   if constexpr (MASK == FLEX_MASK_CAUSAL) {

@@ -28,6 +28,38 @@ struct FwdParams {
   int32_t out_bf16;
 };
 
+// Backward: gradients of q, k and v.  Both block masks are the forward's
+// (kv-major, for dq) and its transpose (q-major, for dk and dv).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;   // the forward's output
+  const void* dout;  // its gradient
+  const float* lse;  // the forward's log-sum-exp (natural log)
+  const float* dlse; // gradient of the log-sum-exp, may be null
+  float* ws;         // [2 * B * H * q_len]: -delta per row, then a per row
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* kv_num;
+  const int32_t* kv_idx;
+  const int32_t* fkv_num;
+  const int32_t* fkv_idx;
+  const int32_t* q_num;
+  const int32_t* q_idx;
+  const int32_t* fq_num;
+  const int32_t* fq_idx;
+  int32_t B, H, q_len, kv_len, n_qb, n_kb;
+  int32_t window, window_min, prefix;
+  float c1;          // |scale| * log2(e)
+  float scale;       // the signed scale (factor of dq and dk)
+  float inv_abs_scale;
+  int32_t neg;       // scale < 0: the sign goes onto q (dq kernel) or k (dk/dv kernel)
+  float bias_max;
+  int32_t grad_bf16;
+};
+
 struct MaskBuildParams {
   int32_t kind, window, window_min, prefix;
   int32_t q_len, kv_len, q_block, kv_block, n_qb, n_kb;
@@ -38,10 +70,17 @@ struct MaskBuildParams {
 };
 
 hipError_t launch_block_mask(const MaskBuildParams& p, hipStream_t stream);
+// The transposed arrays: kv_num / kv_idx / fkv_num / fkv_idx receive
+// q_num_blocks [n_kb], q_indices [n_kb * n_qb], full_q_num_blocks,
+// full_q_indices.
+hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream);
 
 // fwd_supported() decides FLEX_E_UNSUPPORTED before launch_fwd() is called;
 // launch_fwd() returns hipErrorInvalidValue for an instance it does not have.
 bool fwd_supported(int in_dtype, int head_dim, int q_block, int kv_block);
+bool bwd_supported(int in_dtype, int head_dim, int q_block, int kv_block);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, int q_block, int kv_block,
+                      int mask_kind, int score_kind, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int head_dim,
                       int q_block, int kv_block, int mask_kind, int score_kind,
                       bool subtile, hipStream_t stream);

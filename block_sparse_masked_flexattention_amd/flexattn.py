@@ -30,7 +30,10 @@ EXPORTED = (
     "flex_attn_strerror",
     "flex_attn_block_mask_dims",
     "flex_attn_build_block_mask",
+    "flex_attn_build_block_mask_t",
     "flex_attn_fwd",
+    "flex_attn_bwd_workspace_floats",
+    "flex_attn_bwd",
 )
 
 
@@ -52,6 +55,13 @@ class BlockMaskStruct(ctypes.Structure):
                 ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
                 ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
                 ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+
+
+class BlockMaskTStruct(ctypes.Structure):
+    _fields_ = [("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
+                ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
+                ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
+                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
 
 
 class ScoreDesc(ctypes.Structure):
@@ -96,6 +106,18 @@ def load(path: str | None = None):
                                       ctypes.c_float, vp, i32, vp,
                                       ctypes.POINTER(FwdOptions), vp]
         lib.flex_attn_fwd.restype = i32
+        lib.flex_attn_build_block_mask_t.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32,
+                                                     i32, vp, vp, vp, vp, vp]
+        lib.flex_attn_build_block_mask_t.restype = i32
+        lib.flex_attn_bwd_workspace_floats.argtypes = [i32, i32, i32,
+                                                       ctypes.POINTER(ctypes.c_int64)]
+        lib.flex_attn_bwd_workspace_floats.restype = i32
+        lib.flex_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(BlockMaskStruct),
+                                      ctypes.POINTER(BlockMaskTStruct),
+                                      ctypes.POINTER(ScoreDesc), ctypes.c_float, vp, vp, vp,
+                                      i32, vp, vp]
+        lib.flex_attn_bwd.restype = i32
         if lib.flex_attn_abi_version() != ABI_VERSION:
             raise RuntimeError("libflexattn.so ABI version mismatch")
         if path is None:
@@ -223,3 +245,110 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
         lse.data_ptr() if lse is not None else None, ctypes.byref(opt),
         _stream_handle(q.device)), "flex_attn_fwd")
     return out, (lse if return_lse or lse is not None else None)
+
+
+@dataclass
+class BlockMaskT:
+    """The transposed block arrays (per kv-block column), on the device."""
+    mask: dict
+    q_len: int
+    kv_len: int
+    q_block: int
+    kv_block: int
+    q_num_blocks: torch.Tensor       # int32 [nKVB]
+    q_indices: torch.Tensor          # int32 [nKVB, nQB]
+    full_q_num_blocks: torch.Tensor  # int32 [nKVB]
+    full_q_indices: torch.Tensor     # int32 [nKVB, nQB]
+
+    def as_struct(self) -> BlockMaskTStruct:
+        nk, nq = self.q_indices.shape
+        return BlockMaskTStruct(self.q_block, self.kv_block, nq, nk,
+                                self.q_num_blocks.data_ptr(), self.q_indices.data_ptr(),
+                                self.full_q_num_blocks.data_ptr(),
+                                self.full_q_indices.data_ptr())
+
+    def arrays(self):
+        return (self.q_num_blocks, self.q_indices, self.full_q_num_blocks,
+                self.full_q_indices)
+
+
+def build_block_mask_t(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int,
+                       device="cuda", out: BlockMaskT | None = None) -> BlockMaskT:
+    """Build the transposed block arrays on the device (current stream)."""
+    nq, nk = block_mask_dims(q_len, kv_len, q_block, kv_block)
+    if out is None:
+        dev = torch.device(device)
+        z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
+        out = BlockMaskT(dict(mask), q_len, kv_len, q_block, kv_block,
+                         z(nk), z(nk, nq), z(nk), z(nk, nq))
+    arrs = out.arrays()
+    for a, shape in zip(arrs, [(nk,), (nk, nq), (nk,), (nk, nq)]):
+        if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
+            raise ValueError("transposed block-mask arrays have the wrong dtype/shape")
+    md = mask_desc(mask)
+    dev = arrs[0].device
+    _check(load().flex_attn_build_block_mask_t(
+        ctypes.byref(md), q_len, kv_len, q_block, kv_block,
+        *[a.data_ptr() for a in arrs], _stream_handle(dev)), "flex_attn_build_block_mask_t")
+    return out
+
+
+def bwd_workspace_floats(B: int, H: int, q_len: int) -> int:
+    n = ctypes.c_int64()
+    _check(load().flex_attn_bwd_workspace_floats(B, H, q_len, ctypes.byref(n)),
+           "flex_attn_bwd_workspace_floats")
+    return n.value
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+        dout: torch.Tensor, lse: torch.Tensor, block_mask: BlockMask,
+        block_mask_t: BlockMaskT, score: dict | None = None, scale: float | None = None, *,
+        dlse: torch.Tensor | None = None, grad_dtype: torch.dtype | None = None,
+        workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
+        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv) of the masked attention forward.  q/k/v/out/dout
+    as in ``fwd`` (out and lse the forward's results), lse float32 [B,H,Lq]."""
+    B, H, Lq, D = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+        raise ValueError("q/k/v shapes disagree")
+    if out.shape != (B, H, Lq, D) or dout.shape != (B, H, Lq, D):
+        raise ValueError("out/dout shapes disagree with q")
+    if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, out, dout)):
+        raise ValueError("q/k/v/out/dout must share a dtype in {bfloat16, float32}")
+    for t in (q, k, v, out, dout):
+        if not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q/k/v/out/dout must be contiguous GPU tensors")
+    if lse.shape != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("bad lse tensor")
+    if dlse is not None and (dlse.shape != (B, H, Lq) or dlse.dtype != torch.float32
+                             or not dlse.is_contiguous()):
+        raise ValueError("bad dlse tensor")
+    gd = grad_dtype or torch.float32
+    if gd not in _DT:
+        raise ValueError("grad_dtype must be bfloat16 or float32")
+    mk = lambda L: torch.empty((B, H, L, D), dtype=gd, device=q.device)
+    dq = mk(Lq) if dq is None else dq
+    dk = mk(Lk) if dk is None else dk
+    dv = mk(Lk) if dv is None else dv
+    for t, L in ((dq, Lq), (dk, Lk), (dv, Lk)):
+        if t.shape != (B, H, L, D) or t.dtype != gd or not t.is_contiguous():
+            raise ValueError("bad gradient tensor")
+    nws = bwd_workspace_floats(B, H, Lq)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.float32, device=q.device)
+    elif workspace.dtype != torch.float32 or workspace.numel() < nws:
+        raise ValueError("workspace too small")
+    sc = score or {"kind": "identity"}
+    sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
+                   float(sc.get("bias_max", 8.0)))
+    bm = block_mask.as_struct()
+    bmt = block_mask_t.as_struct()
+    scale = default_scale(D) if scale is None else float(scale)
+    _check(load().flex_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+        lse.data_ptr(), dlse.data_ptr() if dlse is not None else None, _DT[q.dtype],
+        B, H, Lq, Lk, D, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _DT[gd], workspace.data_ptr(),
+        _stream_handle(q.device)), "flex_attn_bwd")
+    return dq, dk, dv

@@ -9,7 +9,9 @@ exact same values.
 Recipe: ``torch.Generator("cpu").manual_seed(seed)``; q, k, v drawn in that
 order with ``torch.randn(shape, float32)`` times ``std``; then rounded to
 bfloat16 (round-to-nearest-even) unless the workload is float32.  Tensors are
-contiguous ``[B, H, L, D]``.
+contiguous ``[B, H, L, D]``.  The backward's output gradient (and the optional
+log-sum-exp gradient) come from a second generator seeded ``seed + 7919``:
+dout ~ N(0, 1) of q's shape and dtype, then dlse ~ N(0, 1) float32 [B, H, Lq].
 """
 from __future__ import annotations
 
@@ -75,3 +77,16 @@ def make_inputs(cfg: dict, seed: int | None = None):
     if cfg["dtype"] == "bf16":
         q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
     return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def make_grad_inputs(cfg: dict, with_dlse: bool = False, seed: int | None = None):
+    """dout (the workload's dtype, q's shape) and dlse (float32 [B, H, Lq] or
+    None) as CPU tensors, for the backward."""
+    g = torch.Generator("cpu").manual_seed((cfg["seed"] if seed is None else seed) + 7919)
+    B, H, Lq = cfg["B"], cfg["H"], cfg["q_len"]
+    dv = cfg.get("dv", cfg["d"])
+    dout = torch.randn((B, H, Lq, dv), generator=g, dtype=torch.float32)
+    dlse = torch.randn((B, H, Lq), generator=g, dtype=torch.float32) if with_dlse else None
+    if cfg["dtype"] == "bf16":
+        dout = dout.to(torch.bfloat16)
+    return dout.contiguous(), dlse

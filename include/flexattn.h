@@ -111,6 +111,25 @@ typedef struct flex_block_mask {
   const int32_t* full_kv_indices;    /* device, [n_q_blocks, n_kv_blocks] */
 } flex_block_mask;
 
+/* ---- transposed block mask, as consumed by the backward ----
+ * The same tile classes listed per kv-block column: the q_num_blocks /
+ * q_indices / full_q_num_blocks / full_q_indices fields of the block-mask
+ * tuple passed to the flex_attention higher-order op in the test hunks of
+ * "[Inductor][Flex Attention] Add Subtiling Option for Alpha Scaling".
+ * q_num_blocks[kb] partial q-blocks of column kb are listed ascending at
+ * q_indices[kb * n_q_blocks ...], followed by every other q-block ascending
+ * (each column a permutation of 0 .. n_q_blocks - 1); the same for the full
+ * tiles.  Built by flex_attn_build_block_mask_t.  All pointers are device
+ * pointers owned by the caller. */
+typedef struct flex_block_mask_t {
+  int32_t q_block, kv_block;      /* the forward block mask's block sizes */
+  int32_t n_q_blocks, n_kv_blocks;
+  const int32_t* q_num_blocks;       /* [n_kv_blocks] */
+  const int32_t* q_indices;          /* [n_kv_blocks * n_q_blocks] */
+  const int32_t* full_q_num_blocks;  /* [n_kv_blocks] */
+  const int32_t* full_q_indices;     /* [n_kv_blocks * n_q_blocks] */
+} flex_block_mask_t;
+
 typedef struct flex_fwd_options {
   /* USE_SUBTILING: rescale the output accumulator by alpha in two halves of
    * the head dimension, each just before the P V products that update it.
@@ -148,6 +167,21 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
                                    int32_t* full_kv_num_blocks,
                                    int32_t* full_kv_indices, void* stream);
 
+/* Build the four transposed block arrays (the q_num_blocks / q_indices /
+ * full_q_num_blocks / full_q_indices fields of the block-mask tuple in the
+ * test hunks of the subtiling page) on the device.
+ *   mask, q_len, kv_len, q_block, kv_block: as flex_attn_build_block_mask.
+ *   outputs: device int32 arrays, [n_kv_blocks] and [n_kv_blocks * n_q_blocks];
+ *   every column is written in full (selected q-blocks ascending, then the
+ *   others ascending).
+ * Errors: as flex_attn_build_block_mask. */
+int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
+                                     int32_t kv_len, int32_t q_block,
+                                     int32_t kv_block, int32_t* q_num_blocks,
+                                     int32_t* q_indices,
+                                     int32_t* full_q_num_blocks,
+                                     int32_t* full_q_indices, void* stream);
+
 /* Attention forward.
  *   q [B, H, q_len, head_dim], k [B, H, kv_len, head_dim],
  *   v [B, H, kv_len, head_dim]: contiguous, element type in_dtype, 16-byte
@@ -171,6 +205,44 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       const flex_block_mask* bm, const flex_score_desc* score,
                       float scale, void* out, int32_t out_dtype, float* lse,
                       const flex_fwd_options* opt, void* stream);
+
+/* Host only.  Floats of device workspace flex_attn_bwd needs:
+ * 2 * B * H * q_len.  Errors: FLEX_E_INVALID_ARG (null output, negative size). */
+int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
+                                       int64_t* n_floats);
+
+/* Attention backward: gradients of q, k and v (the outputs of the
+ * flex_attention_backward higher-order op in the test hunks of the subtiling
+ * page, which takes q, k, v, the forward output and log-sum-exp, the output
+ * gradient and a log-sum-exp gradient).  For every visible pair (i, j), with
+ * p_ij = exp(s_ij - lse_i) and delta_i = <dout_i, out_i> - dlse_i:
+ *   ds_ij = p_ij (<dout_i, v_j> - delta_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dout_i.
+ *   q, out, dout [B, H, q_len, head_dim], k, v [B, H, kv_len, head_dim]:
+ *   contiguous, element type in_dtype, 16-byte aligned device pointers; out
+ *   and lse must be the forward's results for these inputs, mask and score.
+ *   lse: fp32 [B, H, q_len] (natural log; -inf for a row that sees no key).
+ *   dlse: NULL (zero) or fp32 [B, H, q_len].
+ *   bm: the forward's block mask; bmt: its transpose (same mask and block
+ *   sizes), both host pointers to structs of device arrays.
+ *   score, scale: as in the forward call.
+ *   dq [B, H, q_len, head_dim], dk, dv [B, H, kv_len, head_dim] of grad_dtype
+ *   (BF16 or FP32), 16-byte aligned, written in full (zero where nothing
+ *   contributes).
+ *   workspace: device fp32, flex_attn_bwd_workspace_floats() floats, owned by
+ *   the caller; its contents on entry are ignored and left undefined.
+ * Built instances: in_dtype BF16, head_dim 64, (q_block, kv_block) in
+ * {(64, 64), (128, 64), (128, 128)}, any mask kind and score kind.
+ * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED (other instances, scale 0
+ * or not finite), FLEX_E_HIP. */
+int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, const float* dlse,
+                      int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
+                      int32_t kv_len, int32_t head_dim, const flex_block_mask* bm,
+                      const flex_block_mask_t* bmt, const flex_score_desc* score,
+                      float scale, void* dq, void* dk, void* dv, int32_t grad_dtype,
+                      float* workspace, void* stream);
 
 #ifdef __cplusplus
 }

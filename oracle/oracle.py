@@ -202,8 +202,9 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
 
 
 def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dlse=None,
-                       threads: int | None = None):
-    """fp64 gradients (dq, dk, dv) of every head.
+                       threads: int | None = None, heads=None):
+    """fp64 gradients (dq, dk, dv) of every head, or of the flat heads
+    b*H + h listed in ``heads`` (the others are left 0).
 
     q: [B, H, Lq, D], k: [B, H, Lkv, D], v: [B, H, Lkv, Dv], dout: [B, H, Lq, Dv]
     float32 arrays (exact values); dlse: [B, H, Lq] or None.  Heads are
@@ -231,7 +232,9 @@ def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dls
     f64p = ctypes.POINTER(ctypes.c_double)
     ptr = lambda a: a.ctypes.data_as(f32p)
     dlp = ptr(dlse) if dlse is not None else None
-    heads = np.arange(B * H, dtype=np.int64)
+    heads = np.arange(B * H, dtype=np.int64) if heads is None else \
+        np.ascontiguousarray(heads, dtype=np.int64)
+    assert np.all((heads >= 0) & (heads < B * H))
 
     def run(t):
         hs = heads[t:t + 1]
@@ -242,11 +245,12 @@ def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dls
             dq.ctypes.data_as(f64p), dk.ctypes.data_as(f64p), dv.ctypes.data_as(f64p))
 
     nthr = threads or _cpu_threads()
-    if nthr == 1 or B * H <= 1:
-        codes = [run(t) for t in range(B * H)]
+    nh = len(heads)
+    if nthr == 1 or nh <= 1:
+        codes = [run(t) for t in range(nh)]
     else:
-        with ThreadPoolExecutor(min(nthr, B * H)) as ex:
-            codes = list(ex.map(run, range(B * H)))
+        with ThreadPoolExecutor(min(nthr, nh)) as ex:
+            codes = list(ex.map(run, range(nh)))
     if any(c != 0 for c in codes):
         raise ValueError("oracle_attention_backward rejected its arguments")
     return dq, dk, dv

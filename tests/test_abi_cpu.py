@@ -109,3 +109,40 @@ def test_fwd_rejects_on_host():
     # empty problems succeed without launching anything
     assert _fwd(B=0, ptr=None, nq=None) == fa.FLEX_OK
     assert _fwd(Lq=0, ptr=None) == fa.FLEX_OK
+
+
+def _bwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
+         score=None, scale=0.125, grad_dtype=fa.DTYPE_FP32, ptr=0x1000, ws=0x1000,
+         t_blocks=None, lse=0x1000):
+    mask = mask or {"kind": "causal"}
+    nq, nk = -(-Lq // qb), -(-Lk // kb)
+    bm = fa.BlockMaskStruct(fa.mask_desc(mask), Lq, Lk, qb, kb, nq, nk, ptr, ptr, ptr, ptr)
+    tq, tk = t_blocks or (qb, kb)
+    bmt = fa.BlockMaskTStruct(tq, tk, nq, nk, ptr, ptr, ptr, ptr)
+    sd = None if score is None else ctypes.byref(score)
+    return fa.load().flex_attn_bwd(ptr, ptr, ptr, ptr, ptr, lse, None, dtype, B, H, Lq, Lk, D,
+                                   ctypes.byref(bm), ctypes.byref(bmt), sd, scale,
+                                   ptr, ptr, ptr, grad_dtype, ws, None)
+
+
+def test_bwd_rejects_on_host():
+    lib = fa.load()
+    n = ctypes.c_int64()
+    assert lib.flex_attn_bwd_workspace_floats(2, 3, 100, ctypes.byref(n)) == fa.FLEX_OK
+    assert n.value == 2 * 2 * 3 * 100
+    assert lib.flex_attn_bwd_workspace_floats(-1, 3, 100, ctypes.byref(n)) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(B=-1) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(dtype=7) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(grad_dtype=7) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(t_blocks=(128, 64)) == fa.FLEX_E_INVALID_ARG    # transposed mask of other blocks
+    assert _bwd(D=128) == fa.FLEX_E_UNSUPPORTED                # no head-dim-128 backward yet
+    assert _bwd(dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # bf16 inputs only
+    assert _bwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
+    assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED
+    assert _bwd(mask={"kind": "prefix_causal", "prefix": -1}) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(score=fa.ScoreDesc(1, 4, 8.0), H=8) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(ptr=0x1008) == fa.FLEX_E_INVALID_ARG           # not 16-byte aligned
+    assert _bwd(ws=None) == fa.FLEX_E_INVALID_ARG              # workspace required
+    assert _bwd(lse=None) == fa.FLEX_E_INVALID_ARG             # lse required
+    # empty problems succeed without launching anything
+    assert _bwd(B=0, ptr=None, ws=None, lse=None) == fa.FLEX_OK

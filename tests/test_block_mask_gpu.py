@@ -65,3 +65,42 @@ def test_random_tiny_shapes():
 ])
 def test_edge_shapes(case):
     _assert_same(*case)
+
+
+# ---- the transposed arrays (per kv-block column), used by the backward ----
+
+
+def _assert_same_t(mask, q_len, kv_len, qb, kb):
+    bmt = fa.build_block_mask_t(mask, q_len, kv_len, qb, kb, device="cuda:0")
+    torch.cuda.synchronize()
+    got = [a.cpu().numpy() for a in bmt.arrays()]
+    ref = oracle.block_mask_t(mask, q_len, kv_len, qb, kb)
+    for name, g, r in zip(["q_num_blocks", "q_indices", "full_q_num_blocks",
+                           "full_q_indices"], got, ref):
+        assert g.dtype == np.int32
+        np.testing.assert_array_equal(g, r, err_msg="%s %s %s" % (name, mask, (q_len, kv_len, qb, kb)))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_block_masks_t(name):
+    cfg = workload(name)
+    _assert_same_t(cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+
+
+def test_random_tiny_shapes_t():
+    for case in _random_cases(80, seed=11):
+        _assert_same_t(*case)
+
+
+@pytest.mark.parametrize("case", [
+    ({"kind": "causal"}, 0, 0, 64, 64),
+    ({"kind": "causal"}, 0, 5, 64, 64),
+    ({"kind": "causal"}, 1, 1, 1, 1),
+    ({"kind": "noop"}, 1000, 1000, 1024, 1024),
+    ({"kind": "causal"}, 1300, 700, 128, 1),
+    ({"kind": "sliding_window", "window": 2000000000, "window_min": 0}, 300, 300, 32, 32),
+    ({"kind": "prefix_causal", "prefix": 0}, 200, 200, 64, 32),
+    ({"kind": "noop"}, 700, 20, 2, 16),  # more q-blocks than threads per work-group
+])
+def test_edge_shapes_t(case):
+    _assert_same_t(*case)

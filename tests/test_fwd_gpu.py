@@ -263,3 +263,13 @@ def test_score_spike_mid_row(dtype):
     vf = v.double().numpy()
     tol = 1e-2 if dtype == "bf16" else 1e-4
     assert np.abs(o[:, :, 150:, :] - vf[:, :, 150:151, :]).max() <= tol
+
+
+@pytest.mark.parametrize("kv_block", [64, 128])
+def test_many_items_per_workgroup(kv_block):
+    """2048 (head, q-block) work-groups, several times what the chip holds at
+    once, each with a short tile list; kv_block 64 gives odd step counts,
+    128 even ones.  Every row is compared."""
+    cfg = workload("prefix_causal", B=16, H=64, q_len=200, kv_len=200,
+                   mask={"kind": "prefix_causal", "prefix": 70}, q_block=128, kv_block=kv_block)
+    _full_compare(cfg, "fp32")
