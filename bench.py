@@ -10,6 +10,14 @@ measured step time; `roofline` reports the forward kernel alone, timed with
 HIP events on the stream it is launched on; `cpu_baseline` times the fp64
 oracle on a bounded sample of rows of the same workload.
 
+`--pass bwd` measures the backward instead: one step = build both block-mask
+arrays (per q-block and per kv-block) on the device, then the backward (the
+per-row delta pass, the dq kernel and the dk/dv kernel) from the forward's
+output and lse, computed once beforehand.  Its `value` counts 10 * D FLOPs per
+visible pair (the five products S, dP, dV, dK, dQ the gradients need, each
+2 * D; the kernels recompute S and dP once more, which is not counted), and
+its `cpu_baseline` times the oracle's backward on whole heads.
+
 `--copy-calibration` instead runs only a plain device-to-device copy of a
 known size, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be
 scaled against it.
@@ -106,6 +114,124 @@ def cpu_baseline(cfg, q, k, v, target_seconds: float, seed: int = 0):
     }
 
 
+def cpu_baseline_bwd(cfg, q, k, v, dout, target_seconds: float):
+    """Time the fp64 oracle backward on whole heads (one per host thread per
+    round) until it has run about `target_seconds`."""
+    from oracle import oracle
+
+    B, H, L, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["d"]
+    qf, kf, vf, df = (t.float().numpy() for t in (q, k, v, dout))
+    threads = oracle.threads_used()
+    per_head = 10.0 * D * visible_pairs(cfg["mask"], L, cfg["kv_len"])
+    spent, flops, heads_done, h0 = 0.0, 0.0, 0, 0
+    while spent < target_seconds and heads_done < B * H:
+        n = min(threads, B * H - h0)
+        heads = np.arange(h0, h0 + n)
+        t0 = time.perf_counter()
+        oracle.attention_backward(qf, kf, vf, df, cfg["mask"], cfg["score"], cfg["scale"],
+                                  threads=threads, heads=heads)
+        spent += time.perf_counter() - t0
+        flops += per_head * n
+        heads_done += n
+        h0 += n
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d whole heads (of %d) of the workload, fp64 oracle backward, %.1f s"
+                  % (heads_done, B * H, spent),
+    }
+
+
+def run_bwd(args, cfg, name, q, k, v):
+    """The backward measurement (see the module docstring)."""
+    import torch
+    from block_sparse_masked_flexattention_amd import flexattn as fa
+    from block_sparse_masked_flexattention_amd.inputs import make_grad_inputs
+
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    dout, _ = make_grad_inputs(cfg)
+    dod = dout.to(dev)
+    B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
+    bargs = (cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"])
+    bm = fa.build_block_mask(*bargs, device=dev)
+    bmt = fa.build_block_mask_t(*bargs, device=dev)
+    out, lse = fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], return_lse=True)
+    gd = qd.dtype
+    dq = torch.empty((B, H, Lq, D), dtype=gd, device=dev)
+    dk = torch.empty((B, H, Lk, D), dtype=gd, device=dev)
+    dv = torch.empty((B, H, Lk, D), dtype=gd, device=dev)
+    ws = torch.empty(max(fa.bwd_workspace_floats(B, H, Lq), 1), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        fa.build_block_mask(*bargs, out=bm)
+        fa.build_block_mask_t(*bargs, out=bmt)
+        if ev is not None:
+            ev[0].record(stream)
+        fa.bwd(qd, kd, vd, out, dod, lse, bm, bmt, cfg["score"], cfg["scale"],
+               grad_dtype=gd, workspace=ws, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    bwd_ms = [a.elapsed_time(b) for a, b in events]
+    bwd_avg_ms = float(np.mean(bwd_ms))
+    pairs = visible_pairs(cfg["mask"], Lq, Lk)
+    flops = 10.0 * B * H * D * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (bwd_avg_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS
+    res = {
+        "metric": "effective TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, flex-attn bwd",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
+            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"], "mask": cfg["mask"],
+            "score_mod": cfg["score"]["kind"], "grad_dtype": cfg["dtype"],
+            "visible_pairs_per_head": pairs,
+            "step": "block-mask build (both layouts) + backward (delta, dq, dk/dv)",
+        },
+        "pct_peak": round(100.0 * value / peak, 2),
+        "bwd_ms": round(bwd_avg_ms, 5),
+        "bwd_ms_min": round(float(np.min(bwd_ms)), 5),
+        "roofline": {
+            "bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernels": "delta pass + dq + dk/dv, timed together",
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_bwd(cfg, q, k, v, dout, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def _row_counts(mask, q_len, kv_len):
     """Visible keys per query row, from each row's visible interval."""
     i = np.arange(q_len, dtype=np.int64)
@@ -179,6 +305,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="measure the forward (default) or the backward")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="forward launches timed after a cache-evicting write (0: skip)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -208,6 +336,12 @@ def main(argv=None):
     fa.load()  # fails loudly if the HIP library is missing
 
     q, k, v = make_inputs(cfg)
+    if args.which == "bwd":
+        if cfg["dtype"] != "bf16" or cfg["d"] != 64:
+            print("the backward covers bf16 inputs with head dim 64; workload %s has %s, d=%d"
+                  % (name, cfg["dtype"], cfg["d"]), file=sys.stderr)
+            return 2
+        return run_bwd(args, cfg, name, q, k, v)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
     out = torch.empty((B, H, Lq, D), dtype=qd.dtype, device=dev)
