@@ -302,6 +302,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--use-subtiling", action="store_true")
+    ap.add_argument("--output-max", action="store_true",
+                    help="forward: also write the row max of the scores (OUTPUT_MAX)")
+    ap.add_argument("--prescale-qk", action="store_true",
+                    help="forward: scale q before Q K^T (PRESCALE_QK)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -346,6 +350,7 @@ def main(argv=None):
     B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
     out = torch.empty((B, H, Lq, D), dtype=qd.dtype, device=dev)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if cfg["lse"] else None
+    mx = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if args.output_max else None
     bm = fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -353,8 +358,8 @@ def main(argv=None):
         fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], out=bm)
         if ev is not None:
             ev[0].record(stream)
-        fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out, lse=lse,
-               use_subtiling=args.use_subtiling)
+        fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out, lse=lse, max_out=mx,
+               use_subtiling=args.use_subtiling, prescale_qk=args.prescale_qk)
         if ev is not None:
             ev[1].record(stream)
 
@@ -411,7 +416,8 @@ def main(argv=None):
             "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
             "q_block": cfg["q_block"], "kv_block": cfg["kv_block"], "mask": cfg["mask"],
             "score_mod": cfg["score"]["kind"], "out_dtype": cfg["dtype"], "lse": cfg["lse"],
-            "use_subtiling": args.use_subtiling, "visible_pairs_per_head": pairs,
+            "use_subtiling": args.use_subtiling, "output_max": args.output_max,
+            "prescale_qk": args.prescale_qk, "visible_pairs_per_head": pairs,
             "step": "block-mask build + forward",
         },
         "pct_peak": round(100.0 * value / peak, 2),

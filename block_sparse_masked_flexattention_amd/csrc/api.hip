@@ -147,7 +147,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t kv_len, int32_t head_dim,
                       const flex_block_mask* bm, const flex_score_desc* score,
                       float scale, void* out, int32_t out_dtype, float* lse,
-                      const flex_fwd_options* opt, void* stream) {
+                      float* max_out, const flex_fwd_options* opt, void* stream) {
   if (!bm) return FLEX_E_INVALID_ARG;
   if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0)
     return FLEX_E_INVALID_ARG;
@@ -186,6 +186,8 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
     return FLEX_E_INVALID_ARG;
   const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
   if (align & 15u) return FLEX_E_INVALID_ARG;
+  if (((uintptr_t)lse | (uintptr_t)max_out) & 3u) return FLEX_E_INVALID_ARG;
+  const flex_fwd_options o = opt ? *opt : flex_fwd_options{0, 0, 0, 0};
 
   FwdParams p;
   p.q = q;
@@ -193,6 +195,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   p.v = v;
   p.out = out;
   p.lse = lse;
+  p.max_out = max_out;
   p.kv_num = bm->kv_num_blocks;
   p.kv_idx = bm->kv_indices;
   p.fkv_num = bm->full_kv_num_blocks;
@@ -210,9 +213,20 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   p.neg_q = scale < 0.f ? 1 : 0;
   p.bias_max = bias_max;
   p.out_bf16 = out_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
-  const bool sub = opt != nullptr && opt->use_subtiling != 0;
+  // PRESCALE_QK: q carries scale * log2 e (sign included); scores come out
+  // of the product in base-2 units
+  p.prescale = o.prescale_qk != 0 ? 1 : 0;
+  p.qscale = (float)((double)scale * 1.44269504088896340736);
+  if (p.prescale) {
+    if (!isfinite(p.qscale) || p.qscale == 0.0f) return FLEX_E_UNSUPPORTED;
+    p.c1 = 1.0f;
+    p.neg_q = 0;
+  }
+  p.safe_rows = o.rows_guaranteed_safe != 0 ? 1 : 0;
+  p.contig = o.blocks_are_contiguous != 0 ? 1 : 0;
+  const int variant = (o.use_subtiling != 0 ? kFwdSubtile : 0) | (max_out ? kFwdExactMax : 0);
   return launch_fwd(p, in_dtype, head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
-                    score_kind, sub, static_cast<hipStream_t>(stream)) == hipSuccess
+                    score_kind, variant, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
 }

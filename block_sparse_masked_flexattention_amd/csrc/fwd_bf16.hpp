@@ -116,7 +116,9 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE, bool SUB>
+// XMAX: the row max is an output (OUTPUT_MAX), so every block takes the
+// exact running-max update of forward_block_mn instead of the lagging offset.
+template <int D, int QB, int KB, int MASK, int SCORE, bool SUB, bool XMAX>
 struct Bf16Fwd {
   static constexpr int NQ = bf16_nq<D, QB, KB>();
   static constexpr int NW = QB / (32 * NQ);  // waves per work-group
@@ -232,6 +234,9 @@ struct Bf16Fwd {
     }
 
     // ---- Q fragments: B operand of S^T = K Q^T ----
+    // q times -1 (negative scale) or scale * log2 e (PRESCALE_QK); times 1
+    // otherwise.  Both signs and 1 are exact in bf16.
+    const float qmul = p.prescale ? p.qscale : (p.neg_q ? -1.0f : 1.0f);
     int qi[NQ];
     u32x4 qf[NQ][D / 16];
 #pragma unroll
@@ -242,7 +247,7 @@ struct Bf16Fwd {
       for (int t = 0; t < D / 16; ++t) {
         qf[c][t] = ok ? ld_global16(qg + (size_t)qi[c] * ROWB + (2 * t + g) * 16)
                       : u32x4{0, 0, 0, 0};
-        if (p.neg_q) qf[c][t] ^= 0x80008000u;
+        qf[c][t] = scale_bf16x8(qf[c][t], qmul);
       }
     }
 
@@ -276,7 +281,10 @@ struct Bf16Fwd {
     auto load_window = [&](int base) {  // raw values; clamped when read
       const int t = min(base + lane, ntiles - 1);
       int v = 0;
-      if (t >= 0) v = t < np ? prow[t] : frow[t - np];
+      if (t >= 0) {
+        if (p.contig) v = t < np ? prow[0] + t : frow[0] + (t - np);
+        else v = t < np ? prow[t] : frow[t - np];
+      }
       return v;
     };
     int win_base = 0;
@@ -457,27 +465,32 @@ struct Bf16Fwd {
         // gives +inf and fails the check).
         float pv[NQ][16], rs[NQ];
         bool bad = false;
+        if constexpr (!XMAX) {
 #pragma unroll
-        for (int c = 0; c < NQ; ++c) {
+          for (int c = 0; c < NQ; ++c) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm[c]);
-          if (partial) mask_block(pv[c], c, kvl, 0.f);
-          rs[c] = sum16(pv[c]);
-          bad |= rs[c] > kPMax;
+            for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm[c]);
+            if (partial) mask_block(pv[c], c, kvl, 0.f);
+            rs[c] = sum16(pv[c]);
+            bad |= rs[c] > kPMax;
+          }
         }
         float alpha[NQ];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) alpha[c] = 1.0f;
-        const bool rescale = __any(bad);  // wave-uniform
+        const bool rescale = XMAX || __any(bad);  // wave-uniform
         if (rescale) {
           // Slow path (a row's first visible keys, or scores that rose by
-          // more than log2 kPMax): recompute the block's scores, raise the
-          // running max of every row of the wave to the block max, rescale
-          // by alpha and exponentiate again.  (The empty asm statement
-          // makes the compiler read K from LDS again instead of keeping the
-          // fast path's fragments live through it.)
-          asm volatile("" ::: "memory");
-          s_block(cur, b, kvl, s);
+          // more than log2 kPMax; every block with XMAX): raise the running
+          // max of every row of the wave to the block max, rescale by alpha
+          // and exponentiate.  Coming from the fast path it first recomputes
+          // the block's scores (the empty asm statement makes the compiler
+          // read K from LDS again instead of keeping the fast path's
+          // fragments live through it).
+          if constexpr (!XMAX) {
+            asm volatile("" ::: "memory");
+            s_block(cur, b, kvl, s);
+          }
 #pragma unroll
           for (int c = 0; c < NQ; ++c) {
             if (partial) mask_block(s[c], c, kvl, -INFINITY);
@@ -566,16 +579,20 @@ struct Bf16Fwd {
       if (n + 2 < nsteps) step(Int<2 % NSTAGE>(), n + 2);
     wait_vmcnt<0>();  // leave no load in flight behind the kernel
 
-    // ---- epilogue: out = acc / l, lse = (m + log2 l) ln 2 ----
+    // ---- epilogue: out = acc / l, lse = (m + log2 l) ln 2, max = m ln 2 ----
+    // (with ROWS_GUARANTEED_SAFE the l = 0 guards are left out)
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       const float l_tot = l_run[c] + xor32(l_run[c]);
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const bool live = p.safe_rows || l_tot > 0.f;
+      const float inv = live ? 1.0f / l_tot : 0.f;
       if (qi[c] < p.q_len) {
         write_out_row<NE>(p, head_q + qi[c], D, g, o[c], inv);
         if (p.lse != nullptr && g == 0)
-          p.lse[head_q + qi[c]] =
-              l_tot > 0.f ? (m_run[c] + log2f(l_tot)) * kLn2 : -INFINITY;
+          p.lse[head_q + qi[c]] = live ? (m_run[c] + log2f(l_tot)) * kLn2 : -INFINITY;
+        if constexpr (XMAX) {
+          if (p.max_out != nullptr && g == 0) p.max_out[head_q + qi[c]] = m_run[c] * kLn2;
+        }
       }
     }
   }

@@ -38,6 +38,20 @@ __device__ inline u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// PRESCALE_QK on a 16-byte piece of a bf16 row: each of the eight values
+// times f in fp32, rounded back to bf16 (round to nearest even).  Word i
+// holds elements 2i (low half) and 2i + 1 (high half).
+__device__ inline u32x4 scale_bf16x8(u32x4 x, float f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(x[i] << 16) * f;
+    const float hi = __uint_as_float(x[i] & 0xffff0000u) * f;
+    r[i] = __builtin_bit_cast(unsigned, bf16x2{(__bf16)lo, (__bf16)hi});
+  }
+  return r;
+}
+
 // swap bits 2 and 3 of a row index (an involution)
 __device__ inline int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);

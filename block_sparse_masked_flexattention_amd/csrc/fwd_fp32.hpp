@@ -57,6 +57,7 @@ struct Fp32Fwd {
                                : u32x4{0, 0, 0, 0};
       if (p.neg_q) raw ^= 0x80000000u;
       qf[u] = __builtin_bit_cast(f32x4, raw);
+      if (p.prescale) qf[u] *= p.qscale;  // PRESCALE_QK (fp32: rounded to fp32)
     }
     int lo, hi;
     row_interval<MASK>(p, qi, lo, hi);
@@ -71,7 +72,8 @@ struct Fp32Fwd {
     const int32_t* prow = p.kv_idx + (size_t)qb * nk;
     const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
     auto tile_kb = [&](int n) {
-      const int v = n < np ? prow[n] : frow[n - np];
+      const int v = p.contig ? (n < np ? prow[0] + n : frow[0] + (n - np))
+                             : (n < np ? prow[n] : frow[n - np]);
       return __builtin_amdgcn_readfirstlane(min(max(v, 0), nk - 1));
     };
 
@@ -215,12 +217,15 @@ struct Fp32Fwd {
       kb_cur = kb_next;
     }
 
+    // the running max is exact here, so the row max is m_run (base 2)
     const float l_tot = l_run + xor32(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    const bool live = p.safe_rows || l_tot > 0.f;
+    const float inv = live ? 1.0f / l_tot : 0.f;
     if (qi < p.q_len) {
       write_out_row<NE>(p, head_q + qi, D, g, o, inv);
       if (p.lse != nullptr && g == 0)
-        p.lse[head_q + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[head_q + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (p.max_out != nullptr && g == 0) p.max_out[head_q + qi] = m_run * kLn2;
     }
   }
 };

@@ -15,7 +15,8 @@ struct FwdParams {
   const void* k;
   const void* v;
   void* out;
-  float* lse;  // may be null
+  float* lse;      // may be null
+  float* max_out;  // may be null: the row max of the visible scores
   const int32_t* kv_num;
   const int32_t* kv_idx;
   const int32_t* fkv_num;
@@ -26,6 +27,12 @@ struct FwdParams {
   int32_t neg_q;   // scale < 0: q is negated on load so c1 stays positive
   float bias_max;  // REL_BIAS: slope_h = 2^(-bias_max * (h + 1) / H)
   int32_t out_bf16;
+  // PRESCALE_QK: q is multiplied by qscale (= scale * log2 e) and rounded to
+  // the input type on load; c1 is then 1 and neg_q 0
+  int32_t prescale;
+  float qscale;
+  int32_t safe_rows;  // ROWS_GUARANTEED_SAFE: no fully masked-row guards
+  int32_t contig;     // BLOCKS_ARE_CONTIGUOUS: list n is first + n
 };
 
 // Backward: gradients of q, k and v.  Both block masks are the forward's
@@ -77,12 +84,16 @@ hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream);
 
 // fwd_supported() decides FLEX_E_UNSUPPORTED before launch_fwd() is called;
 // launch_fwd() returns hipErrorInvalidValue for an instance it does not have.
+// Forward variant bits: subtiled alpha rescale, exact running max (taken
+// when the row max is an output).
+constexpr int kFwdSubtile = 1;
+constexpr int kFwdExactMax = 2;
 bool fwd_supported(int in_dtype, int head_dim, int q_block, int kv_block);
 bool bwd_supported(int in_dtype, int head_dim, int q_block, int kv_block);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, int q_block, int kv_block,
                       int mask_kind, int score_kind, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int head_dim,
                       int q_block, int kv_block, int mask_kind, int score_kind,
-                      bool subtile, hipStream_t stream);
+                      int variant, hipStream_t stream);
 
 }  // namespace flexattn

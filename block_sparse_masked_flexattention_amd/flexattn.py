@@ -22,7 +22,7 @@ FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP = 0, 1, 2, 3
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -70,7 +70,9 @@ class ScoreDesc(ctypes.Structure):
 
 
 class FwdOptions(ctypes.Structure):
-    _fields_ = [("use_subtiling", ctypes.c_int32)]
+    _fields_ = [("use_subtiling", ctypes.c_int32), ("prescale_qk", ctypes.c_int32),
+                ("rows_guaranteed_safe", ctypes.c_int32),
+                ("blocks_are_contiguous", ctypes.c_int32)]
 
 
 _lib = None
@@ -103,7 +105,7 @@ def load(path: str | None = None):
         lib.flex_attn_build_block_mask.restype = i32
         lib.flex_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(BlockMaskStruct), ctypes.POINTER(ScoreDesc),
-                                      ctypes.c_float, vp, i32, vp,
+                                      ctypes.c_float, vp, i32, vp, vp,
                                       ctypes.POINTER(FwdOptions), vp]
         lib.flex_attn_fwd.restype = i32
         lib.flex_attn_build_block_mask_t.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32,
@@ -209,11 +211,15 @@ _DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask,
         score: dict | None = None, scale: float | None = None, *,
         out_dtype: torch.dtype | None = None, return_lse: bool = False,
-        use_subtiling: bool = False, out: torch.Tensor | None = None,
-        lse: torch.Tensor | None = None):
+        return_max: bool = False, use_subtiling: bool = False,
+        prescale_qk: bool = False, rows_guaranteed_safe: bool = False,
+        blocks_are_contiguous: bool = False, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None, max_out: torch.Tensor | None = None):
     """Masked block-sparse attention forward.  q [B,H,Lq,D], k/v [B,H,Lkv,D]
     (bfloat16 or float32, contiguous, on the GPU).  Returns (out, lse) with lse
-    None unless requested."""
+    None unless requested; with ``return_max`` (OUTPUT_MAX) returns
+    (out, lse, max) where max is the float32 [B,H,Lq] row max of the scores.
+    The remaining flags are the kernel options of the same names."""
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
     if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
@@ -233,18 +239,28 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
     if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
                             or not lse.is_contiguous()):
         raise ValueError("bad lse tensor")
+    if return_max and max_out is None:
+        max_out = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if max_out is not None and (max_out.shape != (B, H, Lq) or max_out.dtype != torch.float32
+                                or not max_out.is_contiguous()):
+        raise ValueError("bad max_out tensor")
     sc = score or {"kind": "identity"}
     sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
                    float(sc.get("bias_max", 8.0)))
-    opt = FwdOptions(1 if use_subtiling else 0)
+    opt = FwdOptions(int(bool(use_subtiling)), int(bool(prescale_qk)),
+                     int(bool(rows_guaranteed_safe)), int(bool(blocks_are_contiguous)))
     bm = block_mask.as_struct()
     scale = default_scale(D) if scale is None else float(scale)
     _check(load().flex_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], B, H, Lq, Lk, D,
         ctypes.byref(bm), ctypes.byref(sd), scale, out.data_ptr(), _DT[out.dtype],
-        lse.data_ptr() if lse is not None else None, ctypes.byref(opt),
+        lse.data_ptr() if lse is not None else None,
+        max_out.data_ptr() if max_out is not None else None, ctypes.byref(opt),
         _stream_handle(q.device)), "flex_attn_fwd")
-    return out, (lse if return_lse or lse is not None else None)
+    lse_ret = lse if return_lse or lse is not None else None
+    if return_max or max_out is not None:
+        return out, lse_ret, max_out
+    return out, lse_ret
 
 
 @dataclass

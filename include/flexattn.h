@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 1
+#define FLEXATTN_ABI_VERSION 2
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -130,11 +130,29 @@ typedef struct flex_block_mask_t {
   const int32_t* full_q_indices;     /* [n_kv_blocks * n_q_blocks] */
 } flex_block_mask_t;
 
+/* Forward kernel options: the entries of the kernel_options dict the
+ * flex_attention higher-order op receives in the test hunks of the subtiling
+ * page (all False by default there, and 0 here).  The page names them but
+ * does not define them; the meanings below are the plain readings. */
 typedef struct flex_fwd_options {
   /* USE_SUBTILING: rescale the output accumulator by alpha in two halves of
    * the head dimension, each just before the P V products that update it.
    * Results are bitwise identical either way; only instruction order changes. */
   int32_t use_subtiling;
+  /* PRESCALE_QK: multiply q by scale (times log2 e, the kernel's base-2
+   * units) and round it to the input type once, before Q K^T, instead of
+   * scaling each score.  The scores then carry the rounding of q: for bf16
+   * inputs up to 2^-9 * scale * sum_d |q_d k_d| per score. */
+  int32_t prescale_qk;
+  /* ROWS_GUARANTEED_SAFE: the caller promises that every query row sees at
+   * least one key; the guards that give such a row out = 0 and lse = -inf
+   * are dropped.  A row that sees no key then gets undefined out and lse. */
+  int32_t rows_guaranteed_safe;
+  /* BLOCKS_ARE_CONTIGUOUS: the caller promises that each index list is
+   * consecutive, kv_indices[qb, n] = kv_indices[qb, 0] + n for n below the
+   * count (and the same for full_kv_indices); only the first entry of each
+   * list is read.  Results are undefined (never out of bounds) if not. */
+  int32_t blocks_are_contiguous;
 } flex_fwd_options;
 
 /* Returns FLEXATTN_ABI_VERSION. */
@@ -192,8 +210,13 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
  *   scale: finite and non-zero (pass 1/sqrt(head_dim) for the usual default).
  *   out [B, H, q_len, head_dim] of out_dtype, contiguous, 16-byte aligned.
  *   lse: NULL, or fp32 [B, H, q_len]: natural-log log-sum-exp of the scores
- *   of each row; -inf (and out = 0) for a row that sees no key.
- *   opt: host pointer, NULL = defaults (no subtiling).
+ *   of each row; -inf (and out = 0) for a row that sees no key
+ *   (OUTPUT_LOGSUMEXP of the test hunks).
+ *   max_out: NULL, or fp32 [B, H, q_len]: the largest visible score of each
+ *   row (scaled, after the score modification; -inf for a row that sees no
+ *   key), the third output of the op (OUTPUT_MAX).  Requesting it runs the
+ *   exact running max on every block.
+ *   opt: host pointer, NULL = defaults (every option 0).
  * Built instances: in_dtype BF16 or FP32; head_dim 64 or 128;
  * (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}; any mask kind and
  * score kind; out_dtype BF16 or FP32.  q_len, kv_len >= 0 (ragged last
@@ -204,7 +227,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t kv_len, int32_t head_dim,
                       const flex_block_mask* bm, const flex_score_desc* score,
                       float scale, void* out, int32_t out_dtype, float* lse,
-                      const flex_fwd_options* opt, void* stream);
+                      float* max_out, const flex_fwd_options* opt, void* stream);
 
 /* Host only.  Floats of device workspace flex_attn_bwd needs:
  * 2 * B * H * q_len.  Errors: FLEX_E_INVALID_ARG (null output, negative size). */

@@ -152,15 +152,18 @@ int oracle_block_mask(int kind, int64_t window, int64_t window_min,
  * Attention for a list of query rows.  q is [B, H, q_len, d], k is
  * [B, H, kv_len, d], v is [B, H, kv_len, dv], all contiguous float32 holding
  * the exact input values.  rows[r] is the flat row id (b * H + h) * q_len + i.
- * Writes out[r * dv + c] and lse[r] in fp64.  Returns 0, or -1 on a bad
- * argument or allocation failure.
+ * Writes out[r * dv + c] and lse[r] in fp64, and, when row_max is not NULL,
+ * row_max[r] = the largest visible score of the row (after the score
+ * modification; -inf when the row sees no key), the third output of the
+ * flex_attention op in the subtiling page's test hunks (OUTPUT_MAX).
+ * Returns 0, or -1 on a bad argument or allocation failure.
  */
 int oracle_attention_rows(const float* q, const float* k, const float* v,
                           int64_t B, int64_t H, int64_t q_len, int64_t kv_len,
                           int64_t d, int64_t dv, int mask_kind, int64_t window,
                           int64_t window_min, int64_t prefix, int score_kind,
                           double bias_max, double scale, const int64_t* rows,
-                          int64_t n_rows, double* out, double* lse) {
+                          int64_t n_rows, double* out, double* lse, double* row_max) {
   if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
     return -1;
   if (mask_kind < 0 || mask_kind > 3) return -1;
@@ -206,6 +209,7 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
     }
 
     double* o = out + r * dv;
+    if (row_max) row_max[r] = any ? mx : -INFINITY;
     if (!any) {
       for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
       lse[r] = -INFINITY;

@@ -66,7 +66,7 @@ def _load():
         lib.oracle_block_mask.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = (
             [f32p, f32p, f32p] + [i64] * 6 + [ctypes.c_int, i64, i64, i64]
-            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p]
+            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
         )
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_block_mask_t.argtypes = [ctypes.c_int] + [i64] * 7 + [i32p] * 4
@@ -150,13 +150,14 @@ def _cpu_threads() -> int:
 
 
 def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
-                   threads: int | None = None):
+                   threads: int | None = None, with_max: bool = False):
     """fp64 attention for selected rows.
 
     q: [B, H, Lq, D], k: [B, H, Lkv, D], v: [B, H, Lkv, Dv] float32 arrays (or
     anything numpy turns into float32 without changing values).  ``rows`` is an
     int64 array of flat row ids (b*H + h)*Lq + i; None means every row.
-    Returns (out [n, Dv] float64, lse [n] float64).
+    Returns (out [n, Dv] float64, lse [n] float64), and with ``with_max`` also
+    the row max of the visible scores [n] (-inf for a row with no key).
     """
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -170,6 +171,7 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
     n = rows.shape[0]
     out = np.zeros((n, Dv), np.float64)
     lse = np.zeros(n, np.float64)
+    mx = np.zeros(n, np.float64) if with_max else None
     score_kind = SCORE_KINDS[score.get("kind", "identity")]
     bias_max = float(score.get("bias_max", 8.0))
     lib = _load()
@@ -186,6 +188,7 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
             rows[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), hi - lo,
             out[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
             lse[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            mx[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if with_max else None,
         )
 
     nthr = threads or _cpu_threads()
@@ -198,7 +201,7 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
             codes = list(ex.map(lambda b: run(*b), bounds))
     if any(c != 0 for c in codes):
         raise ValueError("oracle_attention_rows rejected its arguments")
-    return out, lse
+    return (out, lse, mx) if with_max else (out, lse)
 
 
 def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dlse=None,

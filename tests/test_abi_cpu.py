@@ -76,7 +76,7 @@ def test_build_block_mask_rejects_on_host():
 
 def _fwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
          bm_lens=None, score=None, scale=0.125, out_dtype=fa.DTYPE_BF16, ptr=0x1000,
-         nq=None, nk=None):
+         nq=None, nk=None, lse=None, max_out=None, opt=None):
     mask = mask or {"kind": "causal"}
     nq_, nk_ = -(-Lq // qb), -(-Lk // kb)
     lq, lk = bm_lens or (Lq, Lk)
@@ -84,14 +84,15 @@ def _fwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask
                             nq if nq is not None else nq_, nk if nk is not None else nk_,
                             ptr, ptr, ptr, ptr)
     sd = None if score is None else ctypes.byref(score)
+    od = None if opt is None else ctypes.byref(opt)
     return fa.load().flex_attn_fwd(ptr, ptr, ptr, dtype, B, H, Lq, Lk, D, ctypes.byref(bm), sd,
-                                   scale, ptr, out_dtype, None, None, None)
+                                   scale, ptr, out_dtype, lse, max_out, od, None)
 
 
 def test_fwd_rejects_on_host():
     lib = fa.load()
     assert lib.flex_attn_fwd(0x1000, 0x1000, 0x1000, 0, 1, 1, 128, 128, 64, None, None,
-                             0.125, 0x1000, 0, None, None, None) == fa.FLEX_E_INVALID_ARG
+                             0.125, 0x1000, 0, None, None, None, None) == fa.FLEX_E_INVALID_ARG
     assert _fwd(B=-1) == fa.FLEX_E_INVALID_ARG
     assert _fwd(dtype=5) == fa.FLEX_E_INVALID_ARG
     assert _fwd(out_dtype=9) == fa.FLEX_E_INVALID_ARG
@@ -106,6 +107,10 @@ def test_fwd_rejects_on_host():
     assert _fwd(score=fa.ScoreDesc(5, 1, 8.0)) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(ptr=0x1008) == fa.FLEX_E_INVALID_ARG            # not 16-byte aligned
     assert _fwd(ptr=None) == fa.FLEX_E_INVALID_ARG
+    assert _fwd(lse=0x1002) == fa.FLEX_E_INVALID_ARG            # lse not 4-byte aligned
+    assert _fwd(max_out=0x1001) == fa.FLEX_E_INVALID_ARG        # max not 4-byte aligned
+    # PRESCALE_QK: scale * log2 e must stay a finite, non-zero float
+    assert _fwd(scale=3e38, opt=fa.FwdOptions(0, 1, 0, 0)) == fa.FLEX_E_UNSUPPORTED
     # empty problems succeed without launching anything
     assert _fwd(B=0, ptr=None, nq=None) == fa.FLEX_OK
     assert _fwd(Lq=0, ptr=None) == fa.FLEX_OK
