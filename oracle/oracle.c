@@ -17,6 +17,11 @@
  *    the q >= kv half of that same predicate.  The sliding window is the
  *    causal predicate further limited to q - kv <= window; window_min is an
  *    extra lower bound on q - kv (0 for the plain causal window).
+ *    The document kinds stand for a mask_mod that closes over a tensor (the
+ *    op's mask_mod_other_buffers slot, which the subtiling page's test hunks
+ *    show holding a captured tensor): a per-token document id for queries
+ *    and keys, a query seeing exactly the keys of its own document, and with
+ *    DOCUMENT_CAUSAL only those at or before its own position.
  *
  *  - Scores.  s = scale * <q_i, k_j> from the exact input values widened to
  *    fp64, then the score modification is applied to the scaled score.  The
@@ -71,13 +76,19 @@
 #define ORACLE_MASK_CAUSAL 1
 #define ORACLE_MASK_SLIDING_WINDOW 2
 #define ORACLE_MASK_PREFIX_CAUSAL 3
+#define ORACLE_MASK_DOCUMENT 4
+#define ORACLE_MASK_DOCUMENT_CAUSAL 5
 
 #define ORACLE_SCORE_IDENTITY 0
 #define ORACLE_SCORE_REL_BIAS 1
 
-/* Is key j visible from query i?  Positions out of range are never visible. */
+/* Is key j visible from query i?  Positions out of range are never visible.
+ * The document kinds read a per-token document id for every query (q_doc)
+ * and every key (kv_doc): a query sees the keys of its own document (and,
+ * for DOCUMENT_CAUSAL, only those at or before it). */
 static int mask_true(int kind, int64_t window, int64_t window_min,
-                     int64_t prefix, int64_t i, int64_t j, int64_t q_len,
+                     int64_t prefix,
+                     const int32_t* q_doc, const int32_t* kv_doc, int64_t i, int64_t j, int64_t q_len,
                      int64_t kv_len) {
   if (i < 0 || j < 0 || i >= q_len || j >= kv_len) return 0;
   switch (kind) {
@@ -89,34 +100,43 @@ static int mask_true(int kind, int64_t window, int64_t window_min,
       return (i - j >= window_min) && (i - j <= window);
     case ORACLE_MASK_PREFIX_CAUSAL:
       return ((i <= prefix) && (j <= prefix)) || (i >= j);
+    case ORACLE_MASK_DOCUMENT:
+      if (!q_doc || !kv_doc) return -1;
+      return q_doc[i] == kv_doc[j];
+    case ORACLE_MASK_DOCUMENT_CAUSAL:
+      if (!q_doc || !kv_doc) return -1;
+      return (q_doc[i] == kv_doc[j]) && (i >= j);
     default:
       return -1;
   }
 }
 
 int oracle_mask_value(int kind, int64_t window, int64_t window_min,
-                      int64_t prefix, int64_t i, int64_t j, int64_t q_len,
-                      int64_t kv_len) {
-  return mask_true(kind, window, window_min, prefix, i, j, q_len, kv_len);
+                      int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc,
+                      int64_t i, int64_t j, int64_t q_len, int64_t kv_len) {
+  return mask_true(kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len, kv_len);
 }
 
 /* Number of visible (i, j) pairs over the whole q_len x kv_len square. */
 int64_t oracle_count_visible(int kind, int64_t window, int64_t window_min,
-                             int64_t prefix, int64_t q_len, int64_t kv_len) {
+                             int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc,
+                             int64_t q_len, int64_t kv_len) {
+  if (kind >= 4 && (!q_doc || !kv_doc)) return -1;
   int64_t n = 0;
   for (int64_t i = 0; i < q_len; ++i)
     for (int64_t j = 0; j < kv_len; ++j)
-      n += mask_true(kind, window, window_min, prefix, i, j, q_len, kv_len) == 1;
+      n += mask_true(kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len, kv_len) == 1;
   return n;
 }
 
 /* Brute-force block arrays.  Returns 0, or -1 on a bad argument. */
 int oracle_block_mask(int kind, int64_t window, int64_t window_min,
-                      int64_t prefix, int64_t q_len, int64_t kv_len,
+                      int64_t prefix,
+                      const int32_t* q_doc, const int32_t* kv_doc, int64_t q_len, int64_t kv_len,
                       int64_t q_block, int64_t kv_block, int32_t* kv_num_blocks,
                       int32_t* kv_indices, int32_t* full_kv_num_blocks,
                       int32_t* full_kv_indices) {
-  if (kind < 0 || kind > 3 || q_len < 0 || kv_len < 0 || q_block <= 0 ||
+  if (kind < 0 || kind > 5 || (kind >= 4 && (!q_doc || !kv_doc)) || q_len < 0 || kv_len < 0 || q_block <= 0 ||
       kv_block <= 0)
     return -1;
   int64_t nq = (q_len + q_block - 1) / q_block;
@@ -129,7 +149,7 @@ int oracle_block_mask(int kind, int64_t window, int64_t window_min,
       int64_t count = 0;
       for (int64_t i = qb * q_block; i < (qb + 1) * q_block; ++i)
         for (int64_t j = kb * kv_block; j < (kb + 1) * kv_block; ++j)
-          count += mask_true(kind, window, window_min, prefix, i, j, q_len,
+          count += mask_true(kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len,
                              kv_len) == 1;
       cls[kb] = count == 0 ? 0 : (count == q_block * kv_block ? 2 : 1);
     }
@@ -161,12 +181,13 @@ int oracle_block_mask(int kind, int64_t window, int64_t window_min,
 int oracle_attention_rows(const float* q, const float* k, const float* v,
                           int64_t B, int64_t H, int64_t q_len, int64_t kv_len,
                           int64_t d, int64_t dv, int mask_kind, int64_t window,
-                          int64_t window_min, int64_t prefix, int score_kind,
+                          int64_t window_min, int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc, int score_kind,
                           double bias_max, double scale, const int64_t* rows,
                           int64_t n_rows, double* out, double* lse, double* row_max) {
   if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
     return -1;
-  if (mask_kind < 0 || mask_kind > 3) return -1;
+  if (mask_kind < 0 || mask_kind > 5) return -1;
+  if (mask_kind >= 4 && (!q_doc || !kv_doc)) return -1;
   if (score_kind != ORACLE_SCORE_IDENTITY && score_kind != ORACLE_SCORE_REL_BIAS)
     return -1;
   double* s = (double*)malloc(sizeof(double) * (size_t)(kv_len > 0 ? kv_len : 1));
@@ -193,7 +214,7 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
     double mx = -INFINITY;
     int any = 0;
     for (int64_t j = 0; j < kv_len; ++j) {
-      if (mask_true(mask_kind, window, window_min, prefix, i, j, q_len,
+      if (mask_true(mask_kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len,
                     kv_len) != 1) {
         s[j] = -INFINITY;
         continue;
@@ -235,11 +256,12 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
  * full q-blocks ascending, then every other q-block ascending.  Shapes
  * [nKVB] and [nKVB, nQB].  Returns 0, or -1 on a bad argument. */
 int oracle_block_mask_t(int kind, int64_t window, int64_t window_min,
-                        int64_t prefix, int64_t q_len, int64_t kv_len,
+                        int64_t prefix,
+                        const int32_t* q_doc, const int32_t* kv_doc, int64_t q_len, int64_t kv_len,
                         int64_t q_block, int64_t kv_block, int32_t* q_num_blocks,
                         int32_t* q_indices, int32_t* full_q_num_blocks,
                         int32_t* full_q_indices) {
-  if (kind < 0 || kind > 3 || q_len < 0 || kv_len < 0 || q_block <= 0 ||
+  if (kind < 0 || kind > 5 || (kind >= 4 && (!q_doc || !kv_doc)) || q_len < 0 || kv_len < 0 || q_block <= 0 ||
       kv_block <= 0)
     return -1;
   int64_t nq = (q_len + q_block - 1) / q_block;
@@ -251,7 +273,7 @@ int oracle_block_mask_t(int kind, int64_t window, int64_t window_min,
       int64_t count = 0;
       for (int64_t i = qb * q_block; i < (qb + 1) * q_block; ++i)
         for (int64_t j = kb * kv_block; j < (kb + 1) * kv_block; ++j)
-          count += mask_true(kind, window, window_min, prefix, i, j, q_len,
+          count += mask_true(kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len,
                              kv_len) == 1;
       cls[qb] = count == 0 ? 0 : (count == q_block * kv_block ? 2 : 1);
     }
@@ -283,13 +305,14 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
                               const float* dout, const float* dlse, int64_t B,
                               int64_t H, int64_t q_len, int64_t kv_len,
                               int64_t d, int64_t dv, int mask_kind,
-                              int64_t window, int64_t window_min, int64_t prefix,
+                              int64_t window, int64_t window_min, int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc,
                               int score_kind, double bias_max, double scale,
                               const int64_t* heads, int64_t n_heads, double* dq,
                               double* dk, double* dvg) {
   if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
     return -1;
-  if (mask_kind < 0 || mask_kind > 3) return -1;
+  if (mask_kind < 0 || mask_kind > 5) return -1;
+  if (mask_kind >= 4 && (!q_doc || !kv_doc)) return -1;
   if (score_kind != ORACLE_SCORE_IDENTITY && score_kind != ORACLE_SCORE_REL_BIAS)
     return -1;
   size_t nk = (size_t)(kv_len > 0 ? kv_len : 1);
@@ -324,7 +347,7 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
       double mx = -INFINITY;
       int any = 0;
       for (int64_t j = 0; j < kv_len; ++j) {
-        if (mask_true(mask_kind, window, window_min, prefix, i, j, q_len,
+        if (mask_true(mask_kind, window, window_min, prefix, q_doc, kv_doc, i, j, q_len,
                       kv_len) != 1) {
           s[j] = -INFINITY;
           continue;

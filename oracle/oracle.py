@@ -24,7 +24,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _OUT_DIR = os.path.join(_HERE, "_build")
 _LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
 
-MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3}
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
+              "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
 
 _lib = None
@@ -58,21 +59,23 @@ def _load():
             ctypes.POINTER(ctypes.c_double),
             ctypes.POINTER(ctypes.c_int64),
         )
-        lib.oracle_mask_value.argtypes = [ctypes.c_int] + [i64] * 7
+        # mask arguments: kind, window, window_min, prefix, q_doc, kv_doc
+        m = [ctypes.c_int, i64, i64, i64, i32p, i32p]
+        lib.oracle_mask_value.argtypes = m + [i64] * 4
         lib.oracle_mask_value.restype = ctypes.c_int
-        lib.oracle_count_visible.argtypes = [ctypes.c_int] + [i64] * 5
+        lib.oracle_count_visible.argtypes = m + [i64] * 2
         lib.oracle_count_visible.restype = i64
-        lib.oracle_block_mask.argtypes = [ctypes.c_int] + [i64] * 7 + [i32p] * 4
+        lib.oracle_block_mask.argtypes = m + [i64] * 4 + [i32p] * 4
         lib.oracle_block_mask.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = (
-            [f32p, f32p, f32p] + [i64] * 6 + [ctypes.c_int, i64, i64, i64]
+            [f32p, f32p, f32p] + [i64] * 6 + m
             + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
         )
         lib.oracle_attention_rows.restype = ctypes.c_int
-        lib.oracle_block_mask_t.argtypes = [ctypes.c_int] + [i64] * 7 + [i32p] * 4
+        lib.oracle_block_mask_t.argtypes = m + [i64] * 4 + [i32p] * 4
         lib.oracle_block_mask_t.restype = ctypes.c_int
         lib.oracle_attention_backward.argtypes = (
-            [f32p, f32p, f32p, f32p, f32p] + [i64] * 6 + [ctypes.c_int, i64, i64, i64]
+            [f32p, f32p, f32p, f32p, f32p] + [i64] * 6 + m
             + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
         )
         lib.oracle_attention_backward.restype = ctypes.c_int
@@ -80,25 +83,45 @@ def _load():
         return lib
 
 
-def _mask_args(mask: dict):
+def _doc_ptr(ids):
+    """int32 pointer to a copy of a per-token document id array (the pointer
+    keeps the copy alive), or None."""
+    if ids is None:
+        return None
+    if hasattr(ids, "cpu"):
+        ids = ids.cpu().numpy()
+    a = np.ascontiguousarray(ids, dtype=np.int32)
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _mask_args(mask: dict, q_len: int | None = None, kv_len: int | None = None):
     kind = MASK_KINDS[mask["kind"]]
+    if kind >= 4:
+        # the C code reads q_doc[i], kv_doc[j] for every i < q_len, j < kv_len
+        for key, n in (("q_doc", q_len), ("kv_doc", kv_len)):
+            if mask.get(key) is None:
+                raise ValueError("document mask needs %s" % key)
+            if n is not None and len(mask[key]) < n:
+                raise ValueError("%s shorter than the sequence" % key)
     return (
         kind,
         int(mask.get("window", 0)),
         int(mask.get("window_min", 0)),
         int(mask.get("prefix", 0)),
+        _doc_ptr(mask.get("q_doc")),
+        _doc_ptr(mask.get("kv_doc")),
     )
 
 
 def mask_value(mask: dict, i: int, j: int, q_len: int, kv_len: int) -> bool:
-    r = _load().oracle_mask_value(*_mask_args(mask), i, j, q_len, kv_len)
+    r = _load().oracle_mask_value(*_mask_args(mask, q_len, kv_len), i, j, q_len, kv_len)
     if r < 0:
         raise ValueError("bad mask")
     return bool(r)
 
 
 def count_visible(mask: dict, q_len: int, kv_len: int) -> int:
-    return int(_load().oracle_count_visible(*_mask_args(mask), q_len, kv_len))
+    return int(_load().oracle_count_visible(*_mask_args(mask, q_len, kv_len), q_len, kv_len))
 
 
 def block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int):
@@ -114,7 +137,7 @@ def block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: int)
     ]
     ptrs = [a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for a in arrs]
     r = _load().oracle_block_mask(
-        *_mask_args(mask), q_len, kv_len, q_block, kv_block, *ptrs
+        *_mask_args(mask, q_len, kv_len), q_len, kv_len, q_block, kv_block, *ptrs
     )
     if r != 0:
         raise ValueError("oracle_block_mask rejected its arguments")
@@ -135,7 +158,7 @@ def block_mask_t(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block: in
     ]
     ptrs = [a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for a in arrs]
     r = _load().oracle_block_mask_t(
-        *_mask_args(mask), q_len, kv_len, q_block, kv_block, *ptrs
+        *_mask_args(mask, q_len, kv_len), q_len, kv_len, q_block, kv_block, *ptrs
     )
     if r != 0:
         raise ValueError("oracle_block_mask_t rejected its arguments")
@@ -175,7 +198,7 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
     score_kind = SCORE_KINDS[score.get("kind", "identity")]
     bias_max = float(score.get("bias_max", 8.0))
     lib = _load()
-    margs = _mask_args(mask)
+    margs = _mask_args(mask, Lq, Lkv)
     f32p = ctypes.POINTER(ctypes.c_float)
     qp, kp, vp = (a.ctypes.data_as(f32p) for a in (q, k, v))
 
@@ -230,7 +253,7 @@ def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dls
     score_kind = SCORE_KINDS[score.get("kind", "identity")]
     bias_max = float(score.get("bias_max", 8.0))
     lib = _load()
-    margs = _mask_args(mask)
+    margs = _mask_args(mask, Lq, Lkv)
     f32p = ctypes.POINTER(ctypes.c_float)
     f64p = ctypes.POINTER(ctypes.c_double)
     ptr = lambda a: a.ctypes.data_as(f32p)
