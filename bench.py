@@ -144,18 +144,26 @@ def cpu_baseline_bwd(cfg, q, k, v, dout, target_seconds: float):
     }
 
 
+def _printable_mask(mask: dict) -> dict:
+    """The mask for the JSON line: document ids replaced by their count."""
+    out = {k: v for k, v in mask.items() if k not in ("q_doc", "kv_doc")}
+    if "q_doc" in mask:
+        out["documents"] = int(len(np.unique(np.asarray(mask["q_doc"].cpu()))))
+    return out
+
+
 def run_bwd(args, cfg, name, q, k, v):
     """The backward measurement (see the module docstring)."""
     import torch
     from block_sparse_masked_flexattention_amd import flexattn as fa
-    from block_sparse_masked_flexattention_amd.inputs import make_grad_inputs
+    from block_sparse_masked_flexattention_amd.inputs import make_grad_inputs, with_doc_ids
 
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     dout, _ = make_grad_inputs(cfg)
     dod = dout.to(dev)
     B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
-    bargs = (cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"])
+    bargs = (with_doc_ids(cfg, dev), Lq, Lk, cfg["q_block"], cfg["kv_block"])
     bm = fa.build_block_mask(*bargs, device=dev)
     bmt = fa.build_block_mask_t(*bargs, device=dev)
     out, lse = fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], return_lse=True)
@@ -210,7 +218,8 @@ def run_bwd(args, cfg, name, q, k, v):
         "data": "synthetic",
         "config": {
             "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
-            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"], "mask": cfg["mask"],
+            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
+            "mask": _printable_mask(cfg["mask"]),
             "score_mod": cfg["score"]["kind"], "grad_dtype": cfg["dtype"],
             "visible_pairs_per_head": pairs,
             "step": "block-mask build (both layouts) + backward (delta, dq, dk/dv)",
@@ -237,7 +246,15 @@ def _row_counts(mask, q_len, kv_len):
     i = np.arange(q_len, dtype=np.int64)
     lo = np.zeros(q_len, np.int64)
     hi = np.full(q_len, kv_len - 1, np.int64)
-    if mask["kind"] == "causal":
+    if mask["kind"] in ("document", "document_causal"):
+        # sorted ids: a row sees the run of keys with its own id
+        qd = np.asarray(mask["q_doc"].cpu() if hasattr(mask["q_doc"], "cpu") else mask["q_doc"])
+        kd = np.asarray(mask["kv_doc"].cpu() if hasattr(mask["kv_doc"], "cpu") else mask["kv_doc"])
+        lo = np.searchsorted(kd[:kv_len], qd[:q_len], side="left").astype(np.int64)
+        hi = np.searchsorted(kd[:kv_len], qd[:q_len], side="right").astype(np.int64) - 1
+        if mask["kind"] == "document_causal":
+            hi = np.minimum(hi, i)
+    elif mask["kind"] == "causal":
         hi = np.minimum(hi, i)
     elif mask["kind"] == "sliding_window":
         lo = np.maximum(0, i - mask["window"])
@@ -327,7 +344,8 @@ def main(argv=None):
 
     import torch
     from block_sparse_masked_flexattention_amd import flexattn as fa
-    from block_sparse_masked_flexattention_amd.inputs import BENCH_WORKLOAD, make_inputs, workload
+    from block_sparse_masked_flexattention_amd.inputs import (BENCH_WORKLOAD, make_inputs,
+                                                              with_doc_ids, workload)
 
     if args.copy_calibration:
         copy_calibration(1 << 30, 5)
@@ -335,6 +353,7 @@ def main(argv=None):
 
     name = args.workload or BENCH_WORKLOAD
     cfg = workload(name)
+    cfg["mask"] = with_doc_ids(cfg)  # document ids (CPU) for the oracle and the pair count
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fa.load()  # fails loudly if the HIP library is missing
@@ -351,11 +370,12 @@ def main(argv=None):
     out = torch.empty((B, H, Lq, D), dtype=qd.dtype, device=dev)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if cfg["lse"] else None
     mx = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if args.output_max else None
-    bm = fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
+    dmask = with_doc_ids(cfg, dev)
+    bm = fa.build_block_mask(dmask, Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
-        fa.build_block_mask(cfg["mask"], Lq, Lk, cfg["q_block"], cfg["kv_block"], out=bm)
+        fa.build_block_mask(dmask, Lq, Lk, cfg["q_block"], cfg["kv_block"], out=bm)
         if ev is not None:
             ev[0].record(stream)
         fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out, lse=lse, max_out=mx,
@@ -414,7 +434,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
-            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"], "mask": cfg["mask"],
+            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
+            "mask": _printable_mask(cfg["mask"]),
             "score_mod": cfg["score"]["kind"], "out_dtype": cfg["dtype"], "lse": cfg["lse"],
             "use_subtiling": args.use_subtiling, "output_max": args.output_max,
             "prescale_qk": args.prescale_qk, "visible_pairs_per_head": pairs,

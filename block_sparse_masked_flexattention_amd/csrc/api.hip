@@ -26,6 +26,9 @@ bool mask_ok(const flex_mask_desc& m, int32_t* err) {
         return false;
       }
       return true;
+    case FLEX_MASK_DOCUMENT:
+    case FLEX_MASK_DOCUMENT_CAUSAL:
+      return true;
     default:
       *err = FLEX_E_UNSUPPORTED;
       return false;
@@ -71,7 +74,8 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
                                    int32_t kv_block, int32_t* kv_num_blocks,
                                    int32_t* kv_indices,
                                    int32_t* full_kv_num_blocks,
-                                   int32_t* full_kv_indices, void* stream) {
+                                   int32_t* full_kv_indices, int32_t* row_bounds,
+                                   void* stream) {
   if (!mask) return FLEX_E_INVALID_ARG;
   if (q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0 ||
       q_block > 1024 || kv_block > 1024)
@@ -82,6 +86,9 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
   if ((int64_t)nq * nk > INT32_MAX) return FLEX_E_INVALID_ARG;
   if (nq > 0 && (!kv_num_blocks || !full_kv_num_blocks)) return FLEX_E_INVALID_ARG;
   if (nq > 0 && nk > 0 && (!kv_indices || !full_kv_indices)) return FLEX_E_INVALID_ARG;
+  const bool doc = is_document_mask(mask->kind);
+  if (doc && q_len > 0 && (!row_bounds || !mask->q_doc)) return FLEX_E_INVALID_ARG;
+  if (doc && kv_len > 0 && !mask->kv_doc) return FLEX_E_INVALID_ARG;
   if (nq == 0) return FLEX_OK;
 
   MaskBuildParams p;
@@ -99,6 +106,9 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
   p.kv_idx = kv_indices;
   p.fkv_num = full_kv_num_blocks;
   p.fkv_idx = full_kv_indices;
+  p.q_doc = mask->q_doc;
+  p.kv_doc = mask->kv_doc;
+  p.bounds = doc ? row_bounds : nullptr;
   return launch_block_mask(p, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
@@ -109,7 +119,8 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
                                      int32_t kv_block, int32_t* q_num_blocks,
                                      int32_t* q_indices,
                                      int32_t* full_q_num_blocks,
-                                     int32_t* full_q_indices, void* stream) {
+                                     int32_t* full_q_indices, int32_t* col_bounds,
+                                     void* stream) {
   if (!mask) return FLEX_E_INVALID_ARG;
   if (q_len < 0 || kv_len < 0 || q_block <= 0 || kv_block <= 0 ||
       q_block > 1024 || kv_block > 1024)
@@ -120,6 +131,9 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
   if ((int64_t)nq * nk > INT32_MAX) return FLEX_E_INVALID_ARG;
   if (nk > 0 && (!q_num_blocks || !full_q_num_blocks)) return FLEX_E_INVALID_ARG;
   if (nq > 0 && nk > 0 && (!q_indices || !full_q_indices)) return FLEX_E_INVALID_ARG;
+  const bool doc = is_document_mask(mask->kind);
+  if (doc && kv_len > 0 && (!col_bounds || !mask->kv_doc)) return FLEX_E_INVALID_ARG;
+  if (doc && q_len > 0 && !mask->q_doc) return FLEX_E_INVALID_ARG;
   if (nk == 0) return FLEX_OK;
 
   MaskBuildParams p;
@@ -137,6 +151,9 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
   p.kv_idx = q_indices;
   p.fkv_num = full_q_num_blocks;
   p.fkv_idx = full_q_indices;
+  p.q_doc = mask->q_doc;
+  p.kv_doc = mask->kv_doc;
+  p.bounds = doc ? col_bounds : nullptr;
   return launch_block_mask_t(p, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
@@ -187,6 +204,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
   if (align & 15u) return FLEX_E_INVALID_ARG;
   if (((uintptr_t)lse | (uintptr_t)max_out) & 3u) return FLEX_E_INVALID_ARG;
+  if (is_document_mask(bm->mask.kind) && !bm->row_bounds) return FLEX_E_INVALID_ARG;
   const flex_fwd_options o = opt ? *opt : flex_fwd_options{0, 0, 0, 0};
 
   FwdParams p;
@@ -224,6 +242,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   }
   p.safe_rows = o.rows_guaranteed_safe != 0 ? 1 : 0;
   p.contig = o.blocks_are_contiguous != 0 ? 1 : 0;
+  p.bounds = bm->row_bounds;
   const int variant = (o.use_subtiling != 0 ? kFwdSubtile : 0) | (max_out ? kFwdExactMax : 0);
   return launch_fwd(p, in_dtype, head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
                     score_kind, variant, static_cast<hipStream_t>(stream)) == hipSuccess
@@ -295,6 +314,9 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   const uintptr_t align = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out |
                           (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
   if ((align & 15u) || ((uintptr_t)workspace & 3u)) return FLEX_E_INVALID_ARG;
+  if (is_document_mask(bm->mask.kind) &&
+      ((rows > 0 && !bm->row_bounds) || (krows > 0 && !bmt->col_bounds)))
+    return FLEX_E_INVALID_ARG;
 
   BwdParams p;
   p.q = q;
@@ -316,6 +338,8 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   p.q_idx = bmt->q_indices;
   p.fq_num = bmt->full_q_num_blocks;
   p.fq_idx = bmt->full_q_indices;
+  p.bounds = bm->row_bounds;
+  p.col_bounds = bmt->col_bounds;
   p.B = B;
   p.H = H;
   p.q_len = q_len;

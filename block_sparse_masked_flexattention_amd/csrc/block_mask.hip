@@ -56,8 +56,51 @@ __device__ inline RowInterval visible_keys(const MaskBuildParams& p, int i) {
     case FLEX_MASK_PREFIX_CAUSAL:
       hi = min(hi, i <= p.prefix ? max(p.prefix, i) : i);
       break;
+    case FLEX_MASK_DOCUMENT:
+    case FLEX_MASK_DOCUMENT_CAUSAL:
+      // written by doc_bounds_kernel just before, on the same stream
+      lo = p.bounds[2 * (size_t)i];
+      hi = p.bounds[2 * (size_t)i + 1];
+      break;
   }
   return {lo, hi};
+}
+
+// First index t in [0, n) with a[t] >= x (lower) or a[t] > x (upper), n if
+// none, for a non-decreasing a.  On any other array it still ends after at
+// most log2(n) + 1 halvings and reads only a[0 .. n - 1].
+template <bool UPPER>
+__device__ inline int search_i32(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = lo + ((hi - lo) >> 1);
+    const int v = a[mid];
+    if (UPPER ? v <= x : v < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Document masks: for each of the n_own positions, the interval of the other
+// side's positions with the same document id, [lower, upper - 1]; with the
+// causal kind cut at the position itself (keys j <= i for a row, queries
+// i >= j for a column).  out[2t], out[2t + 1] = first, last (empty when
+// first > last).
+__global__ __launch_bounds__(256) void doc_bounds_kernel(const int32_t* own, int n_own,
+                                                         const int32_t* other, int n_other,
+                                                         int causal, int is_row,
+                                                         int32_t* out) {
+  const int t = blockIdx.x * 256 + (int)threadIdx.x;
+  if (t >= n_own) return;
+  const int id = own[t];
+  int lo = search_i32<false>(other, n_other, id);
+  int hi = search_i32<true>(other, n_other, id) - 1;
+  if (causal) {
+    if (is_row) hi = min(hi, t);
+    else lo = max(lo, t);
+  }
+  out[2 * (size_t)t] = lo;
+  out[2 * (size_t)t + 1] = hi;
 }
 
 // Block-wide reductions through wave shuffles and a small LDS array.
@@ -200,10 +243,21 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
         const int r0 = qb * p.q_block;
         const int r1 = min(r0 + p.q_block, p.q_len);
         bool all = r0 + p.q_block <= p.q_len && c_end < p.kv_len, any = false;
-        for (int i = r0; i < r1; ++i) {
-          const RowInterval iv = visible_keys(p, i);
-          all = all && iv.lo <= c0 && iv.hi >= c_end;
-          any = any || (iv.lo <= iv.hi && iv.lo <= c_last && iv.hi >= c0);
+        if (p.kind == FLEX_MASK_DOCUMENT || p.kind == FLEX_MASK_DOCUMENT_CAUSAL) {
+          // the same classes from the columns' query intervals (p.bounds
+          // holds the column bounds here)
+          const int r_end = r0 + p.q_block - 1, r_last = r1 - 1;
+          for (int j = c0; j <= c_last; ++j) {
+            const int clo = p.bounds[2 * (size_t)j], chi = p.bounds[2 * (size_t)j + 1];
+            all = all && clo <= r0 && chi >= r_end;
+            any = any || (clo <= chi && clo <= r_last && chi >= r0);
+          }
+        } else {
+          for (int i = r0; i < r1; ++i) {
+            const RowInterval iv = visible_keys(p, i);
+            all = all && iv.lo <= c0 && iv.hi >= c_end;
+            any = any || (iv.lo <= iv.hi && iv.lo <= c_last && iv.hi >= c0);
+          }
         }
         c = all ? 2 : (any ? 1 : 0);
       }
@@ -230,6 +284,13 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
 
 hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream) {
   if (p.n_kb == 0) return hipSuccess;
+  if (is_document_mask(p.kind)) {
+    hipLaunchKernelGGL(doc_bounds_kernel, dim3((unsigned)((p.kv_len + 255) / 256)), dim3(256), 0,
+                       stream, p.kv_doc, p.kv_len, p.q_doc, p.q_len,
+                       p.kind == FLEX_MASK_DOCUMENT_CAUSAL ? 1 : 0, 0, p.bounds);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(build_block_mask_t_kernel, dim3(p.n_kb), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();
@@ -237,6 +298,13 @@ hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream) {
 
 hipError_t launch_block_mask(const MaskBuildParams& p, hipStream_t stream) {
   if (p.n_qb == 0) return hipSuccess;
+  if (is_document_mask(p.kind)) {
+    hipLaunchKernelGGL(doc_bounds_kernel, dim3((unsigned)((p.q_len + 255) / 256)), dim3(256), 0,
+                       stream, p.q_doc, p.q_len, p.kv_doc, p.kv_len,
+                       p.kind == FLEX_MASK_DOCUMENT_CAUSAL ? 1 : 0, 1, p.bounds);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(build_block_mask_kernel, dim3(p.n_qb), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();

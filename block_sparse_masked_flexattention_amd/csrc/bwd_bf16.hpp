@@ -84,6 +84,10 @@ __device__ inline void col_interval(const BwdParams& p, int kk, int& lo, int& hi
   } else if constexpr (MASK == FLEX_MASK_PREFIX_CAUSAL) {
     // (q <= P and kk <= P) or q >= kk: every q when kk <= P
     lo = kk <= p.prefix ? 0 : kk;
+  } else if constexpr (MASK == FLEX_MASK_DOCUMENT) {
+    // the transposed builder's per-key interval (causal cut included)
+    lo = p.col_bounds[2 * (size_t)kk];
+    hi = p.col_bounds[2 * (size_t)kk + 1];
   }
 }
 
@@ -326,7 +330,7 @@ struct Bf16BwdDq {
         if (partial) {
           const int off = 16 * (r >> 3) + (r & 7);
           bool vis = off <= lim_hi;
-          if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) vis = vis && off >= lim_lo;
+          if constexpr (fwd::two_sided_mask<MASK>()) vis = vis && off >= lim_lo;
           pr = vis ? pr : 0.f;
         }
         ds[r] = pr * (dp[r] + ndelta);
@@ -689,6 +693,9 @@ hipError_t bwd_pick_mask(const BwdParams& p, int mask, int score, hipStream_t s)
       return bwd_pick_score<D, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
     case FLEX_MASK_SLIDING_WINDOW:
       return bwd_pick_score<D, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
+    case FLEX_MASK_DOCUMENT:
+    case FLEX_MASK_DOCUMENT_CAUSAL:
+      return bwd_pick_score<D, QB, KB, FLEX_MASK_DOCUMENT>(p, score, s);
     default:
       return bwd_pick_score<D, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
   }

@@ -97,7 +97,24 @@ __device__ inline void row_interval(const P& p, int qi, int& lo, int& hi) {
     hi = min(hi, qi - p.window_min);
   } else if constexpr (MASK == FLEX_MASK_PREFIX_CAUSAL) {
     hi = min(hi, qi <= p.prefix ? max(p.prefix, qi) : qi);
+  } else if constexpr (MASK == FLEX_MASK_DOCUMENT) {
+    // both document kinds: the builder's per-row interval (causal cut
+    // included); rows past the end see nothing
+    if (qi < p.q_len) {
+      lo = p.bounds[2 * (size_t)qi];
+      hi = p.bounds[2 * (size_t)qi + 1];
+    } else {
+      lo = 1;
+      hi = 0;
+    }
   }
+}
+
+// Masks whose rows' intervals can start after key 0: partial tiles test both
+// ends.
+template <int MASK>
+constexpr bool two_sided_mask() {
+  return MASK == FLEX_MASK_SLIDING_WINDOW || MASK == FLEX_MASK_DOCUMENT;
 }
 
 // Store one query row of O^T accumulators (lane half g) scaled by inv.

@@ -162,7 +162,7 @@ struct Fp32Fwd {
           for (int r = 0; r < 16; ++r) {
             const int off = 32 * b + 16 * (r >> 3) + (r & 7);
             bool vis = off <= lim_hi;
-            if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) vis = vis && off >= lim_lo;
+            if constexpr (two_sided_mask<MASK>()) vis = vis && off >= lim_lo;
             s[b][r] = vis ? s[b][r] : -INFINITY;
           }
       }

@@ -72,6 +72,9 @@ hipError_t pick_mask(const FwdParams& p, int mask, int score, int var, hipStream
       return pick_score<BF16, D, QB, KB, FLEX_MASK_CAUSAL>(p, score, var, s);
     case FLEX_MASK_SLIDING_WINDOW:
       return pick_score<BF16, D, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, var, s);
+    case FLEX_MASK_DOCUMENT:
+    case FLEX_MASK_DOCUMENT_CAUSAL:
+      return pick_score<BF16, D, QB, KB, FLEX_MASK_DOCUMENT>(p, score, var, s);
     default:
       return pick_score<BF16, D, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, var, s);
   }

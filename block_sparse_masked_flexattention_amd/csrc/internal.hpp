@@ -33,6 +33,7 @@ struct FwdParams {
   float qscale;
   int32_t safe_rows;  // ROWS_GUARANTEED_SAFE: no fully masked-row guards
   int32_t contig;     // BLOCKS_ARE_CONTIGUOUS: list n is first + n
+  const int32_t* bounds;  // document masks: [2 * q_len] visible key interval per row
 };
 
 // Backward: gradients of q, k and v.  Both block masks are the forward's
@@ -57,6 +58,8 @@ struct BwdParams {
   const int32_t* q_idx;
   const int32_t* fq_num;
   const int32_t* fq_idx;
+  const int32_t* bounds;      // document masks: [2 * q_len] key interval per query row
+  const int32_t* col_bounds;  // document masks: [2 * kv_len] query interval per key
   int32_t B, H, q_len, kv_len, n_qb, n_kb;
   int32_t window, window_min, prefix;
   float c1;          // |scale| * log2(e)
@@ -74,7 +77,20 @@ struct MaskBuildParams {
   int32_t* kv_idx;
   int32_t* fkv_num;
   int32_t* fkv_idx;
+  // document masks: the id arrays, and the interval array the builder
+  // writes first (row bounds [2 * q_len] for the kv-major arrays, column
+  // bounds [2 * kv_len] for the transposed ones) and then classifies from
+  const int32_t* q_doc;
+  const int32_t* kv_doc;
+  int32_t* bounds;
 };
+
+// The forward and backward kernels have one instance for both document
+// kinds: the intervals come from memory and the causal cut is already in
+// them.
+inline bool is_document_mask(int kind) {
+  return kind == FLEX_MASK_DOCUMENT || kind == FLEX_MASK_DOCUMENT_CAUSAL;
+}
 
 hipError_t launch_block_mask(const MaskBuildParams& p, hipStream_t stream);
 // The transposed arrays: kv_num / kv_idx / fkv_num / fkv_idx receive

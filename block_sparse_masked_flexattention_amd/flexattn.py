@@ -20,9 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libflexattn.so")
 
 FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP = 0, 1, 2, 3
 DTYPE_BF16, DTYPE_FP32 = 0, 1
-MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3}
+MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
+              "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -45,7 +46,8 @@ class FlexAttnError(RuntimeError):
 
 class MaskDesc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("window_min", ctypes.c_int32), ("prefix", ctypes.c_int32)]
+                ("window_min", ctypes.c_int32), ("prefix", ctypes.c_int32),
+                ("q_doc", ctypes.c_void_p), ("kv_doc", ctypes.c_void_p)]
 
 
 class BlockMaskStruct(ctypes.Structure):
@@ -54,14 +56,16 @@ class BlockMaskStruct(ctypes.Structure):
                 ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
                 ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
                 ("kv_num_blocks", ctypes.c_void_p), ("kv_indices", ctypes.c_void_p),
-                ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p)]
+                ("full_kv_num_blocks", ctypes.c_void_p), ("full_kv_indices", ctypes.c_void_p),
+                ("row_bounds", ctypes.c_void_p)]
 
 
 class BlockMaskTStruct(ctypes.Structure):
     _fields_ = [("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
                 ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
                 ("q_num_blocks", ctypes.c_void_p), ("q_indices", ctypes.c_void_p),
-                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p)]
+                ("full_q_num_blocks", ctypes.c_void_p), ("full_q_indices", ctypes.c_void_p),
+                ("col_bounds", ctypes.c_void_p)]
 
 
 class ScoreDesc(ctypes.Structure):
@@ -101,7 +105,7 @@ def load(path: str | None = None):
                                                   ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.flex_attn_block_mask_dims.restype = i32
         lib.flex_attn_build_block_mask.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32, i32,
-                                                   vp, vp, vp, vp, vp]
+                                                   vp, vp, vp, vp, vp, vp]
         lib.flex_attn_build_block_mask.restype = i32
         lib.flex_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(BlockMaskStruct), ctypes.POINTER(ScoreDesc),
@@ -109,7 +113,7 @@ def load(path: str | None = None):
                                       ctypes.POINTER(FwdOptions), vp]
         lib.flex_attn_fwd.restype = i32
         lib.flex_attn_build_block_mask_t.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32,
-                                                     i32, vp, vp, vp, vp, vp]
+                                                     i32, vp, vp, vp, vp, vp, vp]
         lib.flex_attn_build_block_mask_t.restype = i32
         lib.flex_attn_bwd_workspace_floats.argtypes = [i32, i32, i32,
                                                        ctypes.POINTER(ctypes.c_int64)]
@@ -141,9 +145,30 @@ def default_scale(head_dim: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
 
 
-def mask_desc(mask: dict) -> MaskDesc:
+def is_document(mask: dict) -> bool:
+    return mask["kind"] in ("document", "document_causal")
+
+
+def _doc_ptr(mask: dict, key: str, n: int | None):
+    """Device pointer of a document id tensor (int32, contiguous, on the GPU,
+    at least n long), or None."""
+    t = mask.get(key)
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 \
+            or not t.is_contiguous() or t.device.type != "cuda":
+        raise ValueError("%s must be a contiguous int32 GPU tensor" % key)
+    if n is not None and t.numel() < n:
+        raise ValueError("%s is shorter than the sequence" % key)
+    return t.data_ptr()
+
+
+def mask_desc(mask: dict, q_len: int | None = None, kv_len: int | None = None) -> MaskDesc:
+    """The C descriptor.  Document kinds carry their id tensors
+    (``mask["q_doc"]``, ``mask["kv_doc"]``: int32, non-decreasing)."""
     return MaskDesc(MASK_KINDS[mask["kind"]], int(mask.get("window", 0)),
-                    int(mask.get("window_min", 0)), int(mask.get("prefix", 0)))
+                    int(mask.get("window_min", 0)), int(mask.get("prefix", 0)),
+                    _doc_ptr(mask, "q_doc", q_len), _doc_ptr(mask, "kv_doc", kv_len))
 
 
 def block_mask_dims(q_len: int, kv_len: int, q_block: int, kv_block: int):
@@ -170,13 +195,15 @@ class BlockMask:
     kv_indices: torch.Tensor          # int32 [nQB, nKVB]
     full_kv_num_blocks: torch.Tensor  # int32 [nQB]
     full_kv_indices: torch.Tensor     # int32 [nQB, nKVB]
+    row_bounds: torch.Tensor | None = None  # document kinds: int32 [2 * q_len]
 
     def as_struct(self) -> BlockMaskStruct:
         nq, nk = self.kv_indices.shape
         return BlockMaskStruct(
             mask_desc(self.mask), self.q_len, self.kv_len, self.q_block, self.kv_block,
             nq, nk, self.kv_num_blocks.data_ptr(), self.kv_indices.data_ptr(),
-            self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr())
+            self.full_kv_num_blocks.data_ptr(), self.full_kv_indices.data_ptr(),
+            self.row_bounds.data_ptr() if self.row_bounds is not None else None)
 
     def arrays(self):
         return (self.kv_num_blocks, self.kv_indices, self.full_kv_num_blocks,
@@ -192,16 +219,20 @@ def build_block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block
         dev = torch.device(device)
         z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
         out = BlockMask(dict(mask), q_len, kv_len, q_block, kv_block,
-                        z(nq), z(nq, nk), z(nq), z(nq, nk))
+                        z(nq), z(nq, nk), z(nq), z(nq, nk),
+                        z(2 * q_len) if is_document(mask) else None)
     arrs = out.arrays()
     for a, shape in zip(arrs, [(nq,), (nq, nk), (nq,), (nq, nk)]):
         if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
             raise ValueError("block-mask arrays have the wrong dtype/shape")
-    md = mask_desc(mask)
+    if is_document(mask) and (out.row_bounds is None or out.row_bounds.numel() < 2 * q_len):
+        raise ValueError("a document mask needs row_bounds of 2 * q_len")
+    md = mask_desc(mask, q_len, kv_len)
     dev = arrs[0].device
+    rb = out.row_bounds.data_ptr() if out.row_bounds is not None else None
     _check(load().flex_attn_build_block_mask(
         ctypes.byref(md), q_len, kv_len, q_block, kv_block,
-        *[a.data_ptr() for a in arrs], _stream_handle(dev)), "flex_attn_build_block_mask")
+        *[a.data_ptr() for a in arrs], rb, _stream_handle(dev)), "flex_attn_build_block_mask")
     return out
 
 
@@ -275,13 +306,15 @@ class BlockMaskT:
     q_indices: torch.Tensor          # int32 [nKVB, nQB]
     full_q_num_blocks: torch.Tensor  # int32 [nKVB]
     full_q_indices: torch.Tensor     # int32 [nKVB, nQB]
+    col_bounds: torch.Tensor | None = None  # document kinds: int32 [2 * kv_len]
 
     def as_struct(self) -> BlockMaskTStruct:
         nk, nq = self.q_indices.shape
         return BlockMaskTStruct(self.q_block, self.kv_block, nq, nk,
                                 self.q_num_blocks.data_ptr(), self.q_indices.data_ptr(),
                                 self.full_q_num_blocks.data_ptr(),
-                                self.full_q_indices.data_ptr())
+                                self.full_q_indices.data_ptr(),
+                                self.col_bounds.data_ptr() if self.col_bounds is not None else None)
 
     def arrays(self):
         return (self.q_num_blocks, self.q_indices, self.full_q_num_blocks,
@@ -296,16 +329,20 @@ def build_block_mask_t(mask: dict, q_len: int, kv_len: int, q_block: int, kv_blo
         dev = torch.device(device)
         z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
         out = BlockMaskT(dict(mask), q_len, kv_len, q_block, kv_block,
-                         z(nk), z(nk, nq), z(nk), z(nk, nq))
+                         z(nk), z(nk, nq), z(nk), z(nk, nq),
+                         z(2 * kv_len) if is_document(mask) else None)
     arrs = out.arrays()
     for a, shape in zip(arrs, [(nk,), (nk, nq), (nk,), (nk, nq)]):
         if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
             raise ValueError("transposed block-mask arrays have the wrong dtype/shape")
-    md = mask_desc(mask)
+    if is_document(mask) and (out.col_bounds is None or out.col_bounds.numel() < 2 * kv_len):
+        raise ValueError("a document mask needs col_bounds of 2 * kv_len")
+    md = mask_desc(mask, q_len, kv_len)
     dev = arrs[0].device
+    cb = out.col_bounds.data_ptr() if out.col_bounds is not None else None
     _check(load().flex_attn_build_block_mask_t(
         ctypes.byref(md), q_len, kv_len, q_block, kv_block,
-        *[a.data_ptr() for a in arrs], _stream_handle(dev)), "flex_attn_build_block_mask_t")
+        *[a.data_ptr() for a in arrs], cb, _stream_handle(dev)), "flex_attn_build_block_mask_t")
     return out
 
 

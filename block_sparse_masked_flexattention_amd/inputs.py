@@ -1,10 +1,11 @@
 """Seeded synthetic workloads: shapes, mask and score settings, and inputs.
 
-This module holds no attention arithmetic.  It only names the five workloads
+This module holds no attention arithmetic.  It only names the workloads
 (tiny causal; prefix-bidirectional-or-causal; sliding window; long causal with
-a 128-wide head; causal with a relative-position bias) and draws their q, k, v
-tensors from a seeded CPU generator, so the HIP path and the oracle read the
-exact same values.
+a 128-wide head; causal with a relative-position bias; packed documents,
+causal inside each) and draws their q, k, v tensors (and document ids) from
+seeded CPU generators, so the HIP path and the oracle read the exact same
+values.
 
 Recipe: ``torch.Generator("cpu").manual_seed(seed)``; q, k, v drawn in that
 order with ``torch.randn(shape, float32)`` times ``std``; then rounded to
@@ -46,6 +47,13 @@ WORKLOADS = {
         mask={"kind": "causal"}, score={"kind": "rel_bias", "bias_max": 8.0},
         q_block=128, kv_block=128, lse=True, seed=1005,
     ),
+    # packed sequences: documents of seeded random lengths, causal inside each
+    "document_causal": dict(
+        B=2, H=16, q_len=16384, kv_len=16384, d=64, dtype="bf16", std=1.0,
+        mask={"kind": "document_causal"}, score={"kind": "identity"},
+        q_block=128, kv_block=128, lse=False, seed=1006,
+        doc_len_min=128, doc_len_max=3072,
+    ),
 }
 
 # The workload the throughput benchmark runs by default.
@@ -63,6 +71,38 @@ def workload(name: str, **overrides) -> dict:
     cfg.setdefault("scale", default_scale(cfg["d"]))
     cfg["name"] = name
     return cfg
+
+
+def doc_ids(cfg: dict, seed: int | None = None) -> torch.Tensor:
+    """Per-token document ids (int32, CPU, non-decreasing) for a workload
+    with a document mask: lengths drawn uniformly from [doc_len_min,
+    doc_len_max] by a generator seeded ``seed + 104729`` until they cover the
+    sequence; the last document is cut at the end.  Queries and keys share
+    the ids (q_len == kv_len)."""
+    g = torch.Generator("cpu").manual_seed((cfg["seed"] if seed is None else seed) + 104729)
+    L = cfg["q_len"]
+    lo, hi = cfg.get("doc_len_min", 1), cfg.get("doc_len_max", max(1, L))
+    ids = torch.empty(L, dtype=torch.int32)
+    pos, d = 0, 0
+    while pos < L:
+        n = int(torch.randint(lo, hi + 1, (1,), generator=g))
+        ids[pos:pos + n] = d
+        pos += n
+        d += 1
+    return ids
+
+
+def with_doc_ids(cfg: dict, device=None) -> dict:
+    """The workload's mask dict with q_doc / kv_doc filled in (on `device`)
+    for a document mask; the mask unchanged otherwise."""
+    mask = dict(cfg["mask"])
+    if mask["kind"] in ("document", "document_causal"):
+        if "q_doc" not in mask:
+            mask["q_doc"] = mask["kv_doc"] = doc_ids(cfg)
+        if device is not None:
+            mask["q_doc"] = mask["q_doc"].to(device)
+            mask["kv_doc"] = mask["kv_doc"].to(device)
+    return mask
 
 
 def make_inputs(cfg: dict, seed: int | None = None):

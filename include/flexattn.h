@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 2
+#define FLEXATTN_ABI_VERSION 3
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -62,17 +62,29 @@ extern "C" {
  *                   causal sliding window of width window + 1)
  *   PREFIX_CAUSAL   (i <= prefix AND j <= prefix) OR i >= j   (inclusive
  *                   bound, as in the bad.py mask of the templated-attention
- *                   performance issue) */
+ *                   performance issue)
+ *   DOCUMENT        q_doc[i] == kv_doc[j]
+ *   DOCUMENT_CAUSAL q_doc[i] == kv_doc[j] AND i >= j
+ * The document kinds are a mask_mod that closes over a tensor (the op's
+ * mask_mod_other_buffers slot, which the subtiling page's test hunks show
+ * holding a captured tensor): per-token document ids of packed or jagged
+ * sequences.  Both id arrays must be non-decreasing (each document one run
+ * of positions); then every query sees one interval of keys, which the
+ * builder computes once into the block mask's row_bounds. */
 #define FLEX_MASK_NOOP 0
 #define FLEX_MASK_CAUSAL 1
 #define FLEX_MASK_SLIDING_WINDOW 2
 #define FLEX_MASK_PREFIX_CAUSAL 3
+#define FLEX_MASK_DOCUMENT 4
+#define FLEX_MASK_DOCUMENT_CAUSAL 5
 
 typedef struct flex_mask_desc {
   int32_t kind;       /* FLEX_MASK_* */
   int32_t window;     /* SLIDING_WINDOW: largest visible i - j (>= window_min) */
   int32_t window_min; /* SLIDING_WINDOW: smallest visible i - j (>= 0) */
   int32_t prefix;     /* PREFIX_CAUSAL: last index of the bidirectional prefix (>= 0) */
+  const int32_t* q_doc;  /* DOCUMENT*: device int32 [q_len], non-decreasing */
+  const int32_t* kv_doc; /* DOCUMENT*: device int32 [kv_len], non-decreasing */
 } flex_mask_desc;
 
 /* ---- score modifications (score_mod), applied to the SCALED score s ----
@@ -109,6 +121,10 @@ typedef struct flex_block_mask {
   const int32_t* kv_indices;         /* device, [n_q_blocks, n_kv_blocks] */
   const int32_t* full_kv_num_blocks; /* device, [n_q_blocks] */
   const int32_t* full_kv_indices;    /* device, [n_q_blocks, n_kv_blocks] */
+  /* DOCUMENT*: device int32 [2 * q_len], the keys query i sees are
+   * row_bounds[2i] .. row_bounds[2i + 1] (empty when the first is larger),
+   * written by flex_attn_build_block_mask.  NULL for the other kinds. */
+  const int32_t* row_bounds;
 } flex_block_mask;
 
 /* ---- transposed block mask, as consumed by the backward ----
@@ -128,6 +144,10 @@ typedef struct flex_block_mask_t {
   const int32_t* q_indices;          /* [n_kv_blocks * n_q_blocks] */
   const int32_t* full_q_num_blocks;  /* [n_kv_blocks] */
   const int32_t* full_q_indices;     /* [n_kv_blocks * n_q_blocks] */
+  /* DOCUMENT*: device int32 [2 * kv_len], the queries that see key j are
+   * col_bounds[2j] .. col_bounds[2j + 1], written by
+   * flex_attn_build_block_mask_t.  NULL for the other kinds. */
+  const int32_t* col_bounds;
 } flex_block_mask_t;
 
 /* Forward kernel options: the entries of the kernel_options dict the
@@ -176,6 +196,10 @@ int32_t flex_attn_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t q_block
  *   outputs: device int32 arrays, [n_q_blocks] and [n_q_blocks * n_kv_blocks].
  *   Every index row is written in full: the selected kv-blocks in ascending
  *   order, then every other kv-block in ascending order.
+ *   row_bounds: DOCUMENT*: device int32 [2 * q_len], receives each query's
+ *   visible key interval (pass it on in flex_block_mask.row_bounds); may be
+ *   NULL for the other kinds.  The id arrays are read on the device: ids that
+ *   are not non-decreasing give wrong intervals, never out-of-bounds access.
  * Errors: FLEX_E_INVALID_ARG (null pointer with a non-empty output, bad sizes,
  * bad mask parameters), FLEX_E_UNSUPPORTED (unknown mask kind), FLEX_E_HIP. */
 int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
@@ -183,7 +207,8 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
                                    int32_t kv_block, int32_t* kv_num_blocks,
                                    int32_t* kv_indices,
                                    int32_t* full_kv_num_blocks,
-                                   int32_t* full_kv_indices, void* stream);
+                                   int32_t* full_kv_indices, int32_t* row_bounds,
+                                   void* stream);
 
 /* Build the four transposed block arrays (the q_num_blocks / q_indices /
  * full_q_num_blocks / full_q_indices fields of the block-mask tuple in the
@@ -192,13 +217,17 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
  *   outputs: device int32 arrays, [n_kv_blocks] and [n_kv_blocks * n_q_blocks];
  *   every column is written in full (selected q-blocks ascending, then the
  *   others ascending).
+ *   col_bounds: DOCUMENT*: device int32 [2 * kv_len], receives the interval
+ *   of queries that see each key (pass it on in flex_block_mask_t.col_bounds);
+ *   may be NULL for the other kinds.
  * Errors: as flex_attn_build_block_mask. */
 int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
                                      int32_t kv_len, int32_t q_block,
                                      int32_t kv_block, int32_t* q_num_blocks,
                                      int32_t* q_indices,
                                      int32_t* full_q_num_blocks,
-                                     int32_t* full_q_indices, void* stream);
+                                     int32_t* full_q_indices, int32_t* col_bounds,
+                                     void* stream);
 
 /* Attention forward.
  *   q [B, H, q_len, head_dim], k [B, H, kv_len, head_dim],

@@ -53,11 +53,11 @@ def test_block_mask_dims_rejects(args):
     assert e.value.code == fa.FLEX_E_INVALID_ARG
 
 
-def _build(mask, q_len=128, kv_len=128, qb=64, kb=64, ptr=0x1000):
+def _build(mask, q_len=128, kv_len=128, qb=64, kb=64, ptr=0x1000, bounds=None, t=False):
     md = fa.mask_desc(mask) if isinstance(mask, dict) else mask
-    return fa.load().flex_attn_build_block_mask(
-        ctypes.byref(md) if md is not None else None, q_len, kv_len, qb, kb,
-        ptr, ptr, ptr, ptr, None)
+    fn = fa.load().flex_attn_build_block_mask_t if t else fa.load().flex_attn_build_block_mask
+    return fn(ctypes.byref(md) if md is not None else None, q_len, kv_len, qb, kb,
+              ptr, ptr, ptr, ptr, bounds, None)
 
 
 def test_build_block_mask_rejects_on_host():
@@ -70,8 +70,15 @@ def test_build_block_mask_rejects_on_host():
     assert _build({"kind": "prefix_causal", "prefix": -3}) == fa.FLEX_E_INVALID_ARG
     assert _build(fa.MaskDesc(7, 0, 0, 0)) == fa.FLEX_E_UNSUPPORTED
     assert _build({"kind": "causal"}, ptr=None) == fa.FLEX_E_INVALID_ARG
+    # document kinds need their id arrays and the bounds output
+    for t in (False, True):
+        assert _build(fa.MaskDesc(4, 0, 0, 0, None, 0x1000), bounds=0x1000, t=t) == fa.FLEX_E_INVALID_ARG
+        assert _build(fa.MaskDesc(5, 0, 0, 0, 0x1000, None), bounds=0x1000, t=t) == fa.FLEX_E_INVALID_ARG
+        assert _build(fa.MaskDesc(4, 0, 0, 0, 0x1000, 0x1000), bounds=None, t=t) == fa.FLEX_E_INVALID_ARG
+    assert _build(fa.MaskDesc(6, 0, 0, 0)) == fa.FLEX_E_UNSUPPORTED
     # nothing to do: no launch, success
     assert _build({"kind": "causal"}, q_len=0, ptr=None) == fa.FLEX_OK
+    assert _build(fa.MaskDesc(4, 0, 0, 0, None, None), q_len=0, kv_len=0, ptr=None) == fa.FLEX_OK
 
 
 def _fwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
@@ -107,6 +114,7 @@ def test_fwd_rejects_on_host():
     assert _fwd(score=fa.ScoreDesc(5, 1, 8.0)) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(ptr=0x1008) == fa.FLEX_E_INVALID_ARG            # not 16-byte aligned
     assert _fwd(ptr=None) == fa.FLEX_E_INVALID_ARG
+    assert _fwd(mask={"kind": "document"}) == fa.FLEX_E_INVALID_ARG  # no row bounds
     assert _fwd(lse=0x1002) == fa.FLEX_E_INVALID_ARG            # lse not 4-byte aligned
     assert _fwd(max_out=0x1001) == fa.FLEX_E_INVALID_ARG        # max not 4-byte aligned
     # PRESCALE_QK: scale * log2 e must stay a finite, non-zero float

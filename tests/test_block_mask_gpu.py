@@ -4,14 +4,21 @@ import pytest
 import torch
 
 from block_sparse_masked_flexattention_amd import flexattn as fa
-from block_sparse_masked_flexattention_amd.inputs import WORKLOADS, workload
+from block_sparse_masked_flexattention_amd.inputs import WORKLOADS, with_doc_ids, workload
 from oracle import oracle
 
 pytestmark = pytest.mark.gpu
 
 
+def _dev_mask(mask):
+    """Document ids on the GPU for the library (the oracle reads CPU ones)."""
+    if "q_doc" in mask:
+        return dict(mask, q_doc=mask["q_doc"].to("cuda:0"), kv_doc=mask["kv_doc"].to("cuda:0"))
+    return mask
+
+
 def _gpu_arrays(mask, q_len, kv_len, qb, kb):
-    bm = fa.build_block_mask(mask, q_len, kv_len, qb, kb, device="cuda:0")
+    bm = fa.build_block_mask(_dev_mask(mask), q_len, kv_len, qb, kb, device="cuda:0")
     torch.cuda.synchronize()
     return [a.cpu().numpy() for a in bm.arrays()]
 
@@ -28,7 +35,7 @@ def _assert_same(mask, q_len, kv_len, qb, kb):
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_block_masks(name):
     cfg = workload(name)
-    _assert_same(cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+    _assert_same(with_doc_ids(cfg), cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
 
 
 def _random_cases(n, seed):
@@ -71,7 +78,7 @@ def test_edge_shapes(case):
 
 
 def _assert_same_t(mask, q_len, kv_len, qb, kb):
-    bmt = fa.build_block_mask_t(mask, q_len, kv_len, qb, kb, device="cuda:0")
+    bmt = fa.build_block_mask_t(_dev_mask(mask), q_len, kv_len, qb, kb, device="cuda:0")
     torch.cuda.synchronize()
     got = [a.cpu().numpy() for a in bmt.arrays()]
     ref = oracle.block_mask_t(mask, q_len, kv_len, qb, kb)
@@ -84,7 +91,7 @@ def _assert_same_t(mask, q_len, kv_len, qb, kb):
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_block_masks_t(name):
     cfg = workload(name)
-    _assert_same_t(cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+    _assert_same_t(with_doc_ids(cfg), cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
 
 
 def test_random_tiny_shapes_t():

@@ -144,3 +144,16 @@ def test_missing_or_short_ids_are_rejected():
     with pytest.raises(ValueError):
         oracle.count_visible({"kind": "document", "q_doc": np.zeros(3, np.int32),
                               "kv_doc": np.zeros(4, np.int32)}, 4, 4)
+
+
+def test_document_workload_pair_count_closed_form():
+    """Packed causal documents of lengths n_d: sum_d n_d (n_d + 1) / 2 visible
+    pairs (checked on the workload's id recipe at 4096 tokens)."""
+    from block_sparse_masked_flexattention_amd.inputs import with_doc_ids, workload
+    cfg = workload("document_causal", q_len=4096, kv_len=4096)
+    mask = with_doc_ids(cfg)
+    _, counts = np.unique(mask["q_doc"].numpy(), return_counts=True)
+    assert counts.sum() == 4096 and len(counts) > 2
+    want = int((counts * (counts + 1) // 2).sum())
+    assert oracle.count_visible(mask, 4096, 4096) == want
+    assert oracle.count_visible(dict(mask, kind="document"), 4096, 4096) == int((counts ** 2).sum())
