@@ -5,8 +5,8 @@
 One step = the whole hot path over one batch of seeded synthetic input that
 is already resident in HBM: build the block mask on the device, then run the
 forward.  Prints ONE JSON line.  `value` is effective TFLOP/s over unmasked
-FLOPs, 4 * B * H * D * (visible query-key pairs) per step, divided by the
-measured step time; `roofline` reports the forward kernel alone, timed with
+FLOPs, 2 * B * H * (D + Dv) * (visible query-key pairs) per step (4 * D with
+equal head dims), divided by the measured step time; `roofline` reports the forward kernel alone, timed with
 HIP events on the stream it is launched on; `cpu_baseline` times the fp64
 oracle on a bounded sample of rows of the same workload.
 
@@ -97,7 +97,7 @@ def cpu_baseline(cfg, q, k, v, target_seconds: float, seed: int = 0):
                               threads=threads)
         dt = time.perf_counter() - t0
         spent += dt
-        flops += 4.0 * D * float(counts[rows % L].sum())
+        flops += 2.0 * (D + cfg.get("dv", D)) * float(counts[rows % L].sum())
         rows_done += n
         if spent >= target_seconds:
             break
@@ -323,6 +323,8 @@ def main(argv=None):
                     help="forward: also write the row max of the scores (OUTPUT_MAX)")
     ap.add_argument("--prescale-qk", action="store_true",
                     help="forward: scale q before Q K^T (PRESCALE_QK)")
+    ap.add_argument("--v-head-dim", type=int, default=None,
+                    help="forward: value head dim, when it should differ from the workload's head dim")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -352,7 +354,7 @@ def main(argv=None):
         return 0
 
     name = args.workload or BENCH_WORKLOAD
-    cfg = workload(name)
+    cfg = workload(name, **({"dv": args.v_head_dim} if args.v_head_dim else {}))
     cfg["mask"] = with_doc_ids(cfg)  # document ids (CPU) for the oracle and the pair count
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -367,7 +369,8 @@ def main(argv=None):
         return run_bwd(args, cfg, name, q, k, v)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
-    out = torch.empty((B, H, Lq, D), dtype=qd.dtype, device=dev)
+    Dv = cfg.get("dv", D)
+    out = torch.empty((B, H, Lq, Dv), dtype=qd.dtype, device=dev)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if cfg["lse"] else None
     mx = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if args.output_max else None
     dmask = with_doc_ids(cfg, dev)
@@ -413,7 +416,7 @@ def main(argv=None):
         del flush
     fwd_avg_ms = float(np.mean(fwd_ms))
     pairs = visible_pairs(cfg["mask"], Lq, Lk)
-    flops = 4.0 * B * H * D * pairs
+    flops = 2.0 * B * H * (D + Dv) * pairs  # Q K^T and P V
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (fwd_avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_FP32_TFLOPS
@@ -434,7 +437,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
-            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
+            "v_head_dim": Dv, "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
             "mask": _printable_mask(cfg["mask"]),
             "score_mod": cfg["score"]["kind"], "out_dtype": cfg["dtype"], "lse": cfg["lse"],
             "use_subtiling": args.use_subtiling, "output_max": args.output_max,

@@ -161,12 +161,12 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
 
 int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
-                      int32_t kv_len, int32_t head_dim,
+                      int32_t kv_len, int32_t head_dim, int32_t v_head_dim,
                       const flex_block_mask* bm, const flex_score_desc* score,
                       float scale, void* out, int32_t out_dtype, float* lse,
                       float* max_out, const flex_fwd_options* opt, void* stream) {
   if (!bm) return FLEX_E_INVALID_ARG;
-  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0)
+  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0 || v_head_dim <= 0)
     return FLEX_E_INVALID_ARG;
   if (in_dtype != FLEX_DTYPE_BF16 && in_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
   if (out_dtype != FLEX_DTYPE_BF16 && out_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
@@ -189,12 +189,16 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
       bias_max = score->bias_max;
     }
   }
-  if (!fwd_supported(in_dtype, head_dim, bm->q_block, bm->kv_block))
+  if (!fwd_supported(in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block))
     return FLEX_E_UNSUPPORTED;
 
   const int64_t rows = (int64_t)B * H * q_len;
   const int64_t nwg = (int64_t)B * H * bm->n_q_blocks;
-  if (nwg > INT32_MAX || rows * head_dim > ((int64_t)1 << 40)) return FLEX_E_INVALID_ARG;
+  const int64_t krows = (int64_t)B * H * kv_len;
+  if (nwg > INT32_MAX || rows * head_dim > ((int64_t)1 << 40) ||
+      rows * v_head_dim > ((int64_t)1 << 40) || krows * head_dim > ((int64_t)1 << 40) ||
+      krows * v_head_dim > ((int64_t)1 << 40))
+    return FLEX_E_INVALID_ARG;
   if (rows == 0) return FLEX_OK;  // nothing to write
   if (!q || !out) return FLEX_E_INVALID_ARG;
   if (kv_len > 0 && (!k || !v)) return FLEX_E_INVALID_ARG;
@@ -244,8 +248,9 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   p.contig = o.blocks_are_contiguous != 0 ? 1 : 0;
   p.bounds = bm->row_bounds;
   const int variant = (o.use_subtiling != 0 ? kFwdSubtile : 0) | (max_out ? kFwdExactMax : 0);
-  return launch_fwd(p, in_dtype, head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
-                    score_kind, variant, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_fwd(p, in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block,
+                    bm->mask.kind, score_kind, variant,
+                    static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
 }

@@ -118,7 +118,9 @@ __device__ inline void wait_vmcnt() {
 
 // XMAX: the row max is an output (OUTPUT_MAX), so every block takes the
 // exact running-max update of forward_block_mn instead of the lagging offset.
-template <int D, int QB, int KB, int MASK, int SCORE, bool SUB, bool XMAX>
+// DV: the value head dim (V_HEAD_DIM of the pages' kernel), which may differ
+// from the query / key head dim D.
+template <int D, int DV, int QB, int KB, int MASK, int SCORE, bool SUB, bool XMAX>
 struct Bf16Fwd {
   static constexpr int NQ = bf16_nq<D, QB, KB>();
   static constexpr int NW = QB / (32 * NQ);  // waves per work-group
@@ -127,30 +129,36 @@ struct Bf16Fwd {
   static constexpr int NSTAGE = bf16_nstage<D, QB, KB>();  // LDS stage buffers
   static constexpr int SPT = KB / KS;        // steps per block-mask tile
   static constexpr int NBS = KS / 32;        // 32-key blocks per step
-  static constexpr int NE = D / 32;          // 32-column blocks of the head dim
-  static constexpr int ROWB = D * 2;         // bytes per K / V row
-  static constexpr int STAGE = KS * ROWB;    // bytes of K (or V) per step
-  static constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
-  static constexpr int NDMA = KS * CPR / (64 * NW);  // 16-byte loads per lane per step (K or V)
-  static constexpr int DMA_PER_STEP = 2 * NDMA;      // vector-memory instructions per step
+  static constexpr int NE = DV / 32;         // 32-column blocks of the value head dim
+  static constexpr int ROWB = D * 2;         // bytes per K row
+  static constexpr int ROWBV = DV * 2;       // bytes per V row
+  static constexpr int STAGE = KS * ROWB;    // bytes of K per step (V follows at STAGE)
+  static constexpr int STAGEV = KS * ROWBV;  // bytes of V per step
+  static constexpr int CPR = ROWB / 16;      // 16-byte chunks per K row
+  static constexpr int CPRV = ROWBV / 16;    // 16-byte chunks per V row
+  static constexpr int NDMA = KS * CPR / (64 * NW);    // 16-byte K loads per lane per step
+  static constexpr int NDMAV = KS * CPRV / (64 * NW);  // 16-byte V loads per lane per step
+  static constexpr int DMA_PER_STEP = NDMA + NDMAV;    // vector-memory instructions per step
   // Probabilities are taken against a running offset that may lag the row
   // max; a block whose probabilities would exceed kPMax raises it.
   static constexpr float kPMax = 65536.0f;
   // Occupancy the register allocation aims for, in waves per SIMD: 4 for
   // head dim 64 (<= 128 VGPRs), 2 for 128, and never more than the LDS
   // allows (NSTAGE stage buffers of K and V per work-group, 160 KiB per CU).
-  static constexpr int LDS_WAVES = (kLdsBytes / (NSTAGE * 2 * STAGE)) * NW / 4;
+  static constexpr int LDS_WAVES = (kLdsBytes / (NSTAGE * (STAGE + STAGEV))) * NW / 4;
 #ifdef FLEXATTN_WAVES
   static constexpr int REG_WAVES = FLEXATTN_WAVES;
 #else
-  static constexpr int REG_WAVES = D == 64 ? 4 : 2;
+  static constexpr int REG_WAVES = (D == 64 && DV == 64) ? 4 : 2;
 #endif
   static constexpr int WAVES_PER_SIMD =
       LDS_WAVES < 1 ? 1 : (LDS_WAVES < REG_WAVES ? LDS_WAVES : REG_WAVES);
   static_assert(KS == 32 || KS == 64, "step size");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stage count");
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
+  static_assert(NDMAV * 64 * NW == KS * CPRV, "step split (V)");
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert(DV == 64 || DV == 128, "value head dim");
   static_assert((NSTAGE - 2) * DMA_PER_STEP < 64, "vmcnt range");
 
   // K: row m, 16-byte chunk c at chunk c ^ kswz(m)
@@ -159,8 +167,8 @@ struct Bf16Fwd {
   }
   // V: row r, 8-byte unit u at unit u ^ vswz(r) (even, so 16-byte pieces stay whole)
   __device__ static inline int vswz(int r) {
-    return D == 64 ? ((4 * (r & 1)) ^ (8 * ((r >> 1) & 1)))
-                   : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)));
+    return DV == 64 ? ((4 * (r & 1)) ^ (8 * ((r >> 1) & 1)))
+                    : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)));
   }
 
   // pairwise sum of 16 values (depth 4)
@@ -195,10 +203,10 @@ struct Bf16Fwd {
 
   __device__ static void run(const FwdParams& p) {
     // one distinct LDS variable per stage buffer (unused ones are tiny)
-    __shared__ __attribute__((aligned(16))) char sb0[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) char sb1[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) char sb2[NSTAGE > 2 ? 2 * STAGE : 16];
-    __shared__ __attribute__((aligned(16))) char sb3[NSTAGE > 3 ? 2 * STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char sb0[STAGE + STAGEV];
+    __shared__ __attribute__((aligned(16))) char sb1[STAGE + STAGEV];
+    __shared__ __attribute__((aligned(16))) char sb2[NSTAGE > 2 ? STAGE + STAGEV : 16];
+    __shared__ __attribute__((aligned(16))) char sb3[NSTAGE > 3 ? STAGE + STAGEV : 16];
     lds_t* const buf[4] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -215,7 +223,7 @@ struct Bf16Fwd {
     const size_t head_kv = (size_t)bh * p.kv_len;
     const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
     const char* kg = static_cast<const char*>(p.k) + head_kv * ROWB;
-    const char* vg = static_cast<const char*>(p.v) + head_kv * ROWB;
+    const char* vg = static_cast<const char*>(p.v) + head_kv * ROWBV;
 
     // ---- per-lane constant offsets ----
     // K fragment reads: row 32b + lq, chunk 2t + g (kswz depends on lq only)
@@ -230,7 +238,7 @@ struct Bf16Fwd {
       const int r0 = 8 * g + (j >> 2);
 #pragma unroll
       for (int e = 0; e < NE; ++e)
-        vro[e] = STAGE + r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz(r0)) << 3);
+        vro[e] = STAGE + r0 * ROWBV + (((8 * e + 4 * u + (j & 3)) ^ vswz(r0)) << 3);
     }
 
     // ---- Q fragments: B operand of S^T = K Q^T ----
@@ -310,24 +318,32 @@ struct Bf16Fwd {
       const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
       const int rows_left = min(KS, p.kv_len - kv0);  // >= 1
       const char* kt = kg + (size_t)kv0 * ROWB;
-      const char* vt = vg + (size_t)kv0 * ROWB;
+      const char* vt = vg + (size_t)kv0 * ROWBV;
+      // (K and V loads alternate while both have one left: the same order
+      // as one loop over both when the row widths match)
 #pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int sl = (wave * NDMA + j) * 64 + lane;
-        const int r = sl / CPR, q = sl % CPR;
-        const int rk = min((r & ~31) | swap23(r & 31), rows_left - 1);
-        const int rv = min(r, rows_left - 1);
-        // 32-bit unsigned offsets from a uniform base: the SGPR-base form
-        const unsigned ko = (unsigned)(rk * ROWB) + ((unsigned)(q ^ kswz(r)) << 4);
-        const unsigned vo = (unsigned)(rv * ROWB) + ((unsigned)(q ^ (vswz(r) >> 1)) << 4);
-        __builtin_amdgcn_global_load_lds(kt + ko,
-                                         (__attribute__((address_space(3))) void*)(
-                                             dst + (wave * NDMA + j) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + vo,
-                                         (__attribute__((address_space(3))) void*)(
-                                             dst + STAGE + (wave * NDMA + j) * 1024),
-                                         16, 0, 0);
+      for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
+        if (j < NDMA) {
+          const int sl = (wave * NDMA + j) * 64 + lane;
+          const int r = sl / CPR, q = sl % CPR;
+          const int rk = min((r & ~31) | swap23(r & 31), rows_left - 1);
+          // 32-bit unsigned offsets from a uniform base: the SGPR-base form
+          const unsigned ko = (unsigned)(rk * ROWB) + ((unsigned)(q ^ kswz(r)) << 4);
+          __builtin_amdgcn_global_load_lds(kt + ko,
+                                           (__attribute__((address_space(3))) void*)(
+                                               dst + (wave * NDMA + j) * 1024),
+                                           16, 0, 0);
+        }
+        if (j < NDMAV) {
+          const int sl = (wave * NDMAV + j) * 64 + lane;
+          const int r = sl / CPRV, q = sl % CPRV;
+          const int rv = min(r, rows_left - 1);
+          const unsigned vo = (unsigned)(rv * ROWBV) + ((unsigned)(q ^ (vswz(r) >> 1)) << 4);
+          __builtin_amdgcn_global_load_lds(vt + vo,
+                                           (__attribute__((address_space(3))) void*)(
+                                               dst + STAGE + (wave * NDMAV + j) * 1024),
+                                           16, 0, 0);
+        }
       }
     };
 
@@ -387,11 +403,11 @@ struct Bf16Fwd {
     };
     // V^T fragments of block b, half hh, column block e (two transposing reads)
     auto v_frag = [&](const lds_t* cur, int b, int hh, int e) {
-      const lds_t* vp = cur + vro[e] + (32 * b + 16 * hh) * ROWB;
+      const lds_t* vp = cur + vro[e] + (32 * b + 16 * hh) * ROWBV;
       const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4*)vp);
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vp + 4 * ROWB));
+          (__attribute__((address_space(3))) i16x4*)(vp + 4 * ROWBV));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
@@ -587,7 +603,7 @@ struct Bf16Fwd {
       const bool live = p.safe_rows || l_tot > 0.f;
       const float inv = live ? 1.0f / l_tot : 0.f;
       if (qi[c] < p.q_len) {
-        write_out_row<NE>(p, head_q + qi[c], D, g, o[c], inv);
+        write_out_row<NE>(p, head_q + qi[c], DV, g, o[c], inv);
         if (p.lse != nullptr && g == 0)
           p.lse[head_q + qi[c]] = live ? (m_run[c] + log2f(l_tot)) * kLn2 : -INFINITY;
         if constexpr (XMAX) {

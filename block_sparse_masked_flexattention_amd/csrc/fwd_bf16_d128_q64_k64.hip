@@ -1,4 +1,4 @@
 // bf16 inputs, head dim 128, 64x64 tiles: kernel instances of fwd_kernel.hpp.
 #include "fwd_kernel.hpp"
 
-FLEXATTN_FWD_UNIT(launch_fwd_bf16_d128_q64_k64, true, 128, 64, 64)
+FLEXATTN_FWD_UNIT(launch_fwd_bf16_d128_q64_k64, true, 128, 128, 64, 64)

@@ -1,4 +1,4 @@
 // bf16 inputs, head dim 64, 128x64 tiles: kernel instances of fwd_kernel.hpp.
 #include "fwd_kernel.hpp"
 
-FLEXATTN_FWD_UNIT(launch_fwd_bf16_d64_q128_k64, true, 64, 128, 64)
+FLEXATTN_FWD_UNIT(launch_fwd_bf16_d64_q128_k64, true, 64, 64, 128, 64)

@@ -1,4 +1,4 @@
 // fp32 inputs, head dim 128, 128x128 tiles: kernel instances of fwd_kernel.hpp.
 #include "fwd_kernel.hpp"
 
-FLEXATTN_FWD_UNIT(launch_fwd_fp32_d128_q128_k128, false, 128, 128, 128)
+FLEXATTN_FWD_UNIT(launch_fwd_fp32_d128_q128_k128, false, 128, 128, 128, 128)

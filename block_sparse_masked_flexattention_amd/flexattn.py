@@ -23,7 +23,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -107,7 +107,7 @@ def load(path: str | None = None):
         lib.flex_attn_build_block_mask.argtypes = [ctypes.POINTER(MaskDesc), i32, i32, i32, i32,
                                                    vp, vp, vp, vp, vp, vp]
         lib.flex_attn_build_block_mask.restype = i32
-        lib.flex_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
+        lib.flex_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(BlockMaskStruct), ctypes.POINTER(ScoreDesc),
                                       ctypes.c_float, vp, i32, vp, vp,
                                       ctypes.POINTER(FwdOptions), vp]
@@ -246,14 +246,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
         prescale_qk: bool = False, rows_guaranteed_safe: bool = False,
         blocks_are_contiguous: bool = False, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None, max_out: torch.Tensor | None = None):
-    """Masked block-sparse attention forward.  q [B,H,Lq,D], k/v [B,H,Lkv,D]
-    (bfloat16 or float32, contiguous, on the GPU).  Returns (out, lse) with lse
+    """Masked block-sparse attention forward.  q [B,H,Lq,D], k [B,H,Lkv,D],
+    v [B,H,Lkv,Dv] (bfloat16 or float32, contiguous, on the GPU); out is
+    [B,H,Lq,Dv].  Returns (out, lse) with lse
     None unless requested; with ``return_max`` (OUTPUT_MAX) returns
     (out, lse, max) where max is the float32 [B,H,Lq] row max of the scores.
     The remaining flags are the kernel options of the same names."""
     B, H, Lq, D = q.shape
-    Lk = k.shape[2]
-    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+    Lk, Dv = k.shape[2], v.shape[3]
+    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, Dv):
         raise ValueError("q/k/v shapes disagree")
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q/k/v must share a dtype in {bfloat16, float32}")
@@ -262,8 +263,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
             raise ValueError("q/k/v must be contiguous GPU tensors")
     out_dtype = out_dtype or q.dtype
     if out is None:
-        out = torch.empty((B, H, Lq, D), dtype=out_dtype, device=q.device)
-    elif out.shape != (B, H, Lq, D) or out.dtype not in _DT or not out.is_contiguous():
+        out = torch.empty((B, H, Lq, Dv), dtype=out_dtype, device=q.device)
+    elif out.shape != (B, H, Lq, Dv) or out.dtype not in _DT or not out.is_contiguous():
         raise ValueError("bad out tensor")
     if return_lse and lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
@@ -283,7 +284,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
     bm = block_mask.as_struct()
     scale = default_scale(D) if scale is None else float(scale)
     _check(load().flex_attn_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], B, H, Lq, Lk, D,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), _DT[q.dtype], B, H, Lq, Lk, D, Dv,
         ctypes.byref(bm), ctypes.byref(sd), scale, out.data_ptr(), _DT[out.dtype],
         lse.data_ptr() if lse is not None else None,
         max_out.data_ptr() if max_out is not None else None, ctypes.byref(opt),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 3
+#define FLEXATTN_ABI_VERSION 4
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -231,13 +231,14 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
 
 /* Attention forward.
  *   q [B, H, q_len, head_dim], k [B, H, kv_len, head_dim],
- *   v [B, H, kv_len, head_dim]: contiguous, element type in_dtype, 16-byte
- *   aligned device pointers.
+ *   v [B, H, kv_len, v_head_dim]: contiguous, element type in_dtype, 16-byte
+ *   aligned device pointers.  v_head_dim may differ from head_dim (the
+ *   V_HEAD_DIM of the pages' kernel template).
  *   bm: host pointer; bm->q_len / kv_len must equal the call's; its block
  *   sizes select the kernel.  bm->mask is applied on partial tiles.
  *   score: host pointer, NULL = identity.
  *   scale: finite and non-zero (pass 1/sqrt(head_dim) for the usual default).
- *   out [B, H, q_len, head_dim] of out_dtype, contiguous, 16-byte aligned.
+ *   out [B, H, q_len, v_head_dim] of out_dtype, contiguous, 16-byte aligned.
  *   lse: NULL, or fp32 [B, H, q_len]: natural-log log-sum-exp of the scores
  *   of each row; -inf (and out = 0) for a row that sees no key
  *   (OUTPUT_LOGSUMEXP of the test hunks).
@@ -246,14 +247,15 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
  *   key), the third output of the op (OUTPUT_MAX).  Requesting it runs the
  *   exact running max on every block.
  *   opt: host pointer, NULL = defaults (every option 0).
- * Built instances: in_dtype BF16 or FP32; head_dim 64 or 128;
- * (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}; any mask kind and
- * score kind; out_dtype BF16 or FP32.  q_len, kv_len >= 0 (ragged last
+ * Built instances: in_dtype BF16 with head_dim and v_head_dim each 64 or 128,
+ * or FP32 with head_dim = v_head_dim = 64 or 128; (q_block, kv_block) in
+ * {(64, 64), (128, 64), (128, 128)}; any mask kind and score kind; out_dtype
+ * BF16 or FP32.  q_len, kv_len >= 0 (ragged last
  * blocks are fine), B, H >= 0, B * H * n_q_blocks < 2^31.
  * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP. */
 int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
-                      int32_t kv_len, int32_t head_dim,
+                      int32_t kv_len, int32_t head_dim, int32_t v_head_dim,
                       const flex_block_mask* bm, const flex_score_desc* score,
                       float scale, void* out, int32_t out_dtype, float* lse,
                       float* max_out, const flex_fwd_options* opt, void* stream);

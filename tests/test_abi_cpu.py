@@ -83,7 +83,7 @@ def test_build_block_mask_rejects_on_host():
 
 def _fwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
          bm_lens=None, score=None, scale=0.125, out_dtype=fa.DTYPE_BF16, ptr=0x1000,
-         nq=None, nk=None, lse=None, max_out=None, opt=None):
+         nq=None, nk=None, lse=None, max_out=None, opt=None, Dv=None):
     mask = mask or {"kind": "causal"}
     nq_, nk_ = -(-Lq // qb), -(-Lk // kb)
     lq, lk = bm_lens or (Lq, Lk)
@@ -92,13 +92,14 @@ def _fwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask
                             ptr, ptr, ptr, ptr)
     sd = None if score is None else ctypes.byref(score)
     od = None if opt is None else ctypes.byref(opt)
-    return fa.load().flex_attn_fwd(ptr, ptr, ptr, dtype, B, H, Lq, Lk, D, ctypes.byref(bm), sd,
+    return fa.load().flex_attn_fwd(ptr, ptr, ptr, dtype, B, H, Lq, Lk, D, D if Dv is None else Dv,
+                                   ctypes.byref(bm), sd,
                                    scale, ptr, out_dtype, lse, max_out, od, None)
 
 
 def test_fwd_rejects_on_host():
     lib = fa.load()
-    assert lib.flex_attn_fwd(0x1000, 0x1000, 0x1000, 0, 1, 1, 128, 128, 64, None, None,
+    assert lib.flex_attn_fwd(0x1000, 0x1000, 0x1000, 0, 1, 1, 128, 128, 64, 64, None, None,
                              0.125, 0x1000, 0, None, None, None, None) == fa.FLEX_E_INVALID_ARG
     assert _fwd(B=-1) == fa.FLEX_E_INVALID_ARG
     assert _fwd(dtype=5) == fa.FLEX_E_INVALID_ARG
@@ -106,6 +107,9 @@ def test_fwd_rejects_on_host():
     assert _fwd(bm_lens=(64, 128)) == fa.FLEX_E_INVALID_ARG      # mask built for other lengths
     assert _fwd(nq=3) == fa.FLEX_E_INVALID_ARG                   # wrong block count
     assert _fwd(D=96) == fa.FLEX_E_UNSUPPORTED
+    assert _fwd(Dv=96) == fa.FLEX_E_UNSUPPORTED
+    assert _fwd(Dv=0) == fa.FLEX_E_INVALID_ARG
+    assert _fwd(Dv=128, dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # fp32: Dv = D only
     assert _fwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(scale=float("nan")) == fa.FLEX_E_UNSUPPORTED
