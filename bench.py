@@ -323,6 +323,8 @@ def main(argv=None):
                     help="forward: also write the row max of the scores (OUTPUT_MAX)")
     ap.add_argument("--prescale-qk", action="store_true",
                     help="forward: scale q before Q K^T (PRESCALE_QK)")
+    ap.add_argument("--autotune", action="store_true",
+                    help="forward: time every tile shape first and run the fastest")
     ap.add_argument("--v-head-dim", type=int, default=None,
                     help="forward: value head dim, when it should differ from the workload's head dim")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -374,6 +376,12 @@ def main(argv=None):
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if cfg["lse"] else None
     mx = torch.empty((B, H, Lq), dtype=torch.float32, device=dev) if args.output_max else None
     dmask = with_doc_ids(cfg, dev)
+    tuned = None
+    if args.autotune:
+        from block_sparse_masked_flexattention_amd import autotune
+        tuned = autotune.tune_fwd(qd, kd, vd, dmask, cfg["score"], cfg["scale"], reps=10, warmup=3,
+                                  use_subtiling=args.use_subtiling, prescale_qk=args.prescale_qk)
+        cfg["q_block"], cfg["kv_block"] = tuned.q_block, tuned.kv_block
     bm = fa.build_block_mask(dmask, Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -442,6 +450,9 @@ def main(argv=None):
             "score_mod": cfg["score"]["kind"], "out_dtype": cfg["dtype"], "lse": cfg["lse"],
             "use_subtiling": args.use_subtiling, "output_max": args.output_max,
             "prescale_qk": args.prescale_qk, "visible_pairs_per_head": pairs,
+            "autotune": None if tuned is None else {
+                "chosen": [tuned.q_block, tuned.kv_block],
+                "ms": {"%dx%d" % qk: round(t, 5) for qk, t in tuned.ms.items()}},
             "step": "block-mask build + forward",
         },
         "pct_peak": round(100.0 * value / peak, 2),

@@ -1,0 +1,73 @@
+"""Block-size autotuning: candidate shapes and cache keys on the CPU; on the
+GPU, every candidate is timed, the winner is one of them, a second call is
+served from the cache, and the forward with the chosen tiles meets the usual
+parity bars against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_masked_flexattention_amd import autotune as at
+from block_sparse_masked_flexattention_amd import flexattn as fa
+
+
+def _t(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_candidates():
+    q, v = _t((1, 1, 8, 64)), _t((1, 1, 8, 64))
+    assert at.candidates(q, v) == [(64, 64), (128, 64), (128, 128)]
+    assert at.candidates(q, _t((1, 1, 8, 128))) == [(64, 64), (128, 64), (128, 128)]
+    assert at.candidates(_t((1, 1, 8, 96)), v) == []
+    # fp32 inputs: equal head dims only
+    assert at.candidates(_t((1, 1, 8, 64), torch.float32), _t((1, 1, 8, 128), torch.float32)) == []
+
+
+def test_signature_separates_what_matters():
+    q, k, v = _t((1, 2, 100, 64)), _t((1, 2, 120, 64)), _t((1, 2, 120, 64))
+    s = lambda m, sc=None, **kw: at.signature(q, k, v, m, sc, kw)
+    causal = {"kind": "causal"}
+    assert s(causal) == s(dict(causal))
+    assert s(causal) != s({"kind": "noop"})
+    assert s({"kind": "sliding_window", "window": 10}) != s({"kind": "sliding_window", "window": 11})
+    assert s(causal) != s(causal, {"kind": "rel_bias", "bias_max": 8.0})
+    assert s(causal) != s(causal, use_subtiling=True)
+    ids = torch.tensor([0, 0, 1], dtype=torch.int32)
+    d1 = {"kind": "document", "q_doc": ids, "kv_doc": ids}
+    d2 = {"kind": "document", "q_doc": ids.clone(), "kv_doc": ids.clone()}
+    d3 = {"kind": "document", "q_doc": torch.tensor([0, 1, 1], dtype=torch.int32), "kv_doc": ids}
+    assert s(d1) == s(d2) and s(d1) != s(d3)
+    q2 = _t((1, 2, 101, 64))
+    assert at.signature(q2, k, v, causal, None, {}) != s(causal)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over", [
+    ("prefix_causal", dict(B=1, H=4, q_len=1000, kv_len=1000, mask={"kind": "prefix_causal", "prefix": 300})),
+    ("sliding_window", dict(B=1, H=4, q_len=2000, kv_len=2000)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=900, kv_len=900)),
+])
+def test_tune_and_parity(name, over):
+    from block_sparse_masked_flexattention_amd.inputs import make_inputs, workload
+    from parity import compare, oracle_rows
+    at.clear_cache()
+    cfg = workload(name, **over)
+    q, k, v = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    res = at.tune_fwd(qd, kd, vd, cfg["mask"], cfg["score"], cfg["scale"], reps=3, warmup=1)
+    print(name, res, flush=True)
+    assert set(res.ms) == set(at.TILE_SHAPES)
+    assert all(t > 0 for t in res.ms.values())
+    assert (res.q_block, res.kv_block) in at.TILE_SHAPES and not res.cached
+    again = at.tune_fwd(qd, kd, vd, cfg["mask"], cfg["score"], cfg["scale"])
+    assert again.cached and (again.q_block, again.kv_block) == (res.q_block, res.kv_block)
+    bm = fa.build_block_mask(cfg["mask"], cfg["q_len"], cfg["kv_len"], res.q_block, res.kv_block,
+                             device=dev)
+    out, lse = fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out_dtype=torch.float32,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_rows(cfg, q, k, v)
+    D = cfg["d"]
+    compare(out.double().cpu().numpy().reshape(-1, D), lse.double().cpu().numpy().reshape(-1),
+            ref_out, ref_lse, cfg["dtype"], "fp32", what="tuned " + name)
