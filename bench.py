@@ -364,9 +364,9 @@ def main(argv=None):
 
     q, k, v = make_inputs(cfg)
     if args.which == "bwd":
-        if cfg["dtype"] != "bf16" or cfg["d"] != 64:
-            print("the backward covers bf16 inputs with head dim 64; workload %s has %s, d=%d"
-                  % (name, cfg["dtype"], cfg["d"]), file=sys.stderr)
+        if cfg["dtype"] != "bf16" or cfg["d"] not in (64, 128) or cfg.get("dv", cfg["d"]) != cfg["d"]:
+            print("the backward covers bf16 inputs with head dim 64 or 128 (value head dim equal); "
+                  "workload %s has %s, d=%d" % (name, cfg["dtype"], cfg["d"]), file=sys.stderr)
             return 2
         return run_bwd(args, cfg, name, q, k, v)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))

@@ -175,7 +175,9 @@ struct Bf16BwdDq {
   static constexpr int STAGE = KS * ROWB;   // bytes of K (or V) per step
   static constexpr int CPR = ROWB / 16;
   static constexpr int NDMA = KS * CPR / (64 * NW);
-  static constexpr int WAVES_PER_SIMD = 2;
+  // head dim 128 with 64-row tiles: the extra load addresses of the
+  // two-wave work-group leave room for one wave per SIMD
+  static constexpr int WAVES_PER_SIMD = (D == 128 && QB == 64) ? 1 : 2;
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
 
   __device__ static void run(const BwdParams& p) {
@@ -398,7 +400,9 @@ struct Bf16BwdDkv {
   static constexpr int STAGEB = ARR + 2 * QS * 4;
   static constexpr int CPR = ROWB / 16;
   static constexpr int NDMA = QS * CPR / (64 * NW);
-  static constexpr int WAVES_PER_SIMD = 2;
+  // head dim 128: the wave's K and V rows (64 VGPRs) and the dk and dv
+  // accumulators (128) leave no room for a second wave's registers
+  static constexpr int WAVES_PER_SIMD = D == 64 ? 2 : 1;
   static_assert(NDMA * 64 * NW == QS * CPR, "step split");
 
   __device__ static void run(const BwdParams& p) {

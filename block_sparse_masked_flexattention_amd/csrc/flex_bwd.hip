@@ -5,25 +5,48 @@
 
 namespace flexattn {
 
+typedef hipError_t (*BwdUnit)(const BwdParams&, int, int, hipStream_t);
+
 hipError_t launch_bwd_bf16_d64_q64_k64(const BwdParams&, int, int, hipStream_t);
 hipError_t launch_bwd_bf16_d64_q128_k64(const BwdParams&, int, int, hipStream_t);
 hipError_t launch_bwd_bf16_d64_q128_k128(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_bf16_d128_q64_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_bf16_d128_q128_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_bf16_d128_q128_k128(const BwdParams&, int, int, hipStream_t);
+
+namespace {
+
+struct BwdInstance {
+  int d, qb, kb;
+  BwdUnit fn;
+};
+
+const BwdInstance kBwdInstances[] = {
+    {64, 64, 64, launch_bwd_bf16_d64_q64_k64},
+    {64, 128, 64, launch_bwd_bf16_d64_q128_k64},
+    {64, 128, 128, launch_bwd_bf16_d64_q128_k128},
+    {128, 64, 64, launch_bwd_bf16_d128_q64_k64},
+    {128, 128, 64, launch_bwd_bf16_d128_q128_k64},
+    {128, 128, 128, launch_bwd_bf16_d128_q128_k128},
+};
+
+BwdUnit find_bwd(int head_dim, int q_block, int kv_block) {
+  for (const BwdInstance& b : kBwdInstances)
+    if (b.d == head_dim && b.qb == q_block && b.kb == kv_block) return b.fn;
+  return nullptr;
+}
+
+}  // namespace
 
 bool bwd_supported(int in_dtype, int head_dim, int q_block, int kv_block) {
-  if (in_dtype != FLEX_DTYPE_BF16 || head_dim != 64) return false;
-  return (q_block == 64 && kv_block == 64) || (q_block == 128 && kv_block == 64) ||
-         (q_block == 128 && kv_block == 128);
+  return in_dtype == FLEX_DTYPE_BF16 && find_bwd(head_dim, q_block, kv_block) != nullptr;
 }
 
 hipError_t launch_bwd(const BwdParams& p, int head_dim, int q_block, int kv_block,
                       int mask_kind, int score_kind, hipStream_t stream) {
-  if (head_dim == 64 && q_block == 64 && kv_block == 64)
-    return launch_bwd_bf16_d64_q64_k64(p, mask_kind, score_kind, stream);
-  if (head_dim == 64 && q_block == 128 && kv_block == 64)
-    return launch_bwd_bf16_d64_q128_k64(p, mask_kind, score_kind, stream);
-  if (head_dim == 64 && q_block == 128 && kv_block == 128)
-    return launch_bwd_bf16_d64_q128_k128(p, mask_kind, score_kind, stream);
-  return hipErrorInvalidValue;
+  const BwdUnit fn = find_bwd(head_dim, q_block, kv_block);
+  if (!fn) return hipErrorInvalidValue;
+  return fn(p, mask_kind, score_kind, stream);
 }
 
 }  // namespace flexattn

@@ -286,7 +286,7 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
  *   contributes).
  *   workspace: device fp32, flex_attn_bwd_workspace_floats() floats, owned by
  *   the caller; its contents on entry are ignored and left undefined.
- * Built instances: in_dtype BF16, head_dim 64, (q_block, kv_block) in
+ * Built instances: in_dtype BF16, head_dim 64 or 128, (q_block, kv_block) in
  * {(64, 64), (128, 64), (128, 128)}, any mask kind and score kind.
  * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED (other instances, scale 0
  * or not finite), FLEX_E_HIP. */

@@ -152,7 +152,7 @@ def test_bwd_rejects_on_host():
     assert _bwd(dtype=7) == fa.FLEX_E_INVALID_ARG
     assert _bwd(grad_dtype=7) == fa.FLEX_E_INVALID_ARG
     assert _bwd(t_blocks=(128, 64)) == fa.FLEX_E_INVALID_ARG    # transposed mask of other blocks
-    assert _bwd(D=128) == fa.FLEX_E_UNSUPPORTED                # no head-dim-128 backward yet
+    assert _bwd(D=96) == fa.FLEX_E_UNSUPPORTED                 # head dims 64 and 128 only
     assert _bwd(dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # bf16 inputs only
     assert _bwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED

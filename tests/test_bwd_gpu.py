@@ -121,6 +121,16 @@ SMALL = [
                            q_block=128, kv_block=128)),
     ("tiny_causal", dict(q_len=1, kv_len=1)),
     ("tiny_causal", dict(q_len=33, kv_len=97, mask={"kind": "noop"})),
+    # head dim 128, every tile shape
+    ("long_causal_d128", dict(B=1, H=2, q_len=300, kv_len=300)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=520, kv_len=520, q_block=128, kv_block=64,
+                              mask={"kind": "prefix_causal", "prefix": 200})),
+    ("long_causal_d128", dict(B=1, H=1, q_len=333, kv_len=333, q_block=64, kv_block=64,
+                              mask={"kind": "sliding_window", "window": 90, "window_min": 2})),
+    ("long_causal_d128", dict(B=1, H=4, q_len=260, kv_len=260,
+                              score={"kind": "rel_bias", "bias_max": 8.0})),
+    ("long_causal_d128", dict(B=1, H=1, q_len=200, kv_len=450, mask={"kind": "noop"},
+                              q_block=128, kv_block=64)),
 ]
 
 
@@ -129,13 +139,13 @@ def test_small_parity(name, over):
     _case(name, over)
 
 
-@pytest.mark.parametrize("i", [0, 2, 6, 8])
+@pytest.mark.parametrize("i", [0, 2, 6, 8, 15, 17])
 def test_small_parity_bf16_grads(i):
     name, over = SMALL[i]
     _case(name, over, grad_dtype=torch.bfloat16)
 
 
-@pytest.mark.parametrize("i", [3, 6, 9])
+@pytest.mark.parametrize("i", [3, 6, 9, 16, 18])
 def test_lse_gradient(i):
     name, over = SMALL[i]
     _case(name, over, with_dlse=True)
@@ -208,6 +218,18 @@ def test_full_size_sampled_heads(name):
     # the oracle only on those heads' slices
     ref = oracle_bwd(cfg, q, k, v, dout, heads=heads)
     check(got, ref, torch.float32, "full " + name, heads=heads)
+
+
+def test_long_causal_d128_4k_sampled_heads():
+    """The head-dim-128 workload's settings at 4096 tokens, first and last head."""
+    cfg = workload("long_causal_d128", q_len=4096, kv_len=4096)
+    q, k, v = make_inputs(cfg)
+    dout, dlse = make_grad_inputs(cfg, with_dlse=True)
+    print("case d128 4k", flush=True)
+    got = run_bwd(cfg, q, k, v, dout, dlse)
+    heads = [0, cfg["B"] * cfg["H"] - 1]
+    ref = oracle_bwd(cfg, q, k, v, dout, dlse, heads=heads)
+    check(got, ref, torch.float32, "d128 4k", heads=heads)
 
 
 def test_rel_bias_4k():
