@@ -218,14 +218,18 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildPar
 
 // Transposed arrays (q_num_blocks / q_indices / full_q_num_blocks /
 // full_q_indices, the second half of the same block-mask tuple): one
-// work-group per kv-block column, one thread per (q-block, kv-block) tile.
-// The thread classifies its tile from the q-block's row intervals exactly as
+// work-group per kv-block column, eight lanes per (q-block, kv-block) tile.
+// The lanes classify their tile from the q-block's row intervals exactly as
 // above (full: every row in range and its interval covering the in-range
 // tile; partial: some row's interval meeting the tile's columns), then the
 // same two-pass prefix count orders the column: selected q-blocks ascending,
 // then the others ascending.  The kv_num / kv_idx / fkv_num / fkv_idx fields
 // of the parameters carry the four transposed arrays here.
 __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildParams p) {
+  // kLanes consecutive lanes share a tile and split its rows (or, for the
+  // document kinds, its columns); their verdicts meet through shuffles
+  constexpr int kLanes = 8;
+  constexpr int kTiles = kThreads / kLanes;  // tiles per pass over the column
   __shared__ int scratch[kWaves];
   const int kb = blockIdx.x;
   const int nq = p.n_qb;
@@ -233,38 +237,46 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
   const int c0 = kb * p.kv_block;
   const int c_end = c0 + p.kv_block - 1;
   const int c_last = min(c_end, p.kv_len - 1);  // c0 <= kv_len - 1 since kb < n_kb
+  const int sub = (int)threadIdx.x % kLanes;
+  const bool doc = p.kind == FLEX_MASK_DOCUMENT || p.kind == FLEX_MASK_DOCUMENT_CAUSAL;
   int n_part = 0, n_full = 0;
   for (int pass = 0; pass < 2; ++pass) {
     int seen_part = 0, seen_full = 0;
-    for (int q00 = 0; q00 < nq; q00 += kThreads) {
-      const int qb = q00 + (int)threadIdx.x;
-      int c = 0;  // 0 empty, 1 partial, 2 full
+    for (int q00 = 0; q00 < nq; q00 += kTiles) {
+      const int qb = q00 + (int)threadIdx.x / kLanes;
+      int all = 1, any = 0;
       if (qb < nq) {
         const int r0 = qb * p.q_block;
         const int r1 = min(r0 + p.q_block, p.q_len);
-        bool all = r0 + p.q_block <= p.q_len && c_end < p.kv_len, any = false;
-        if (p.kind == FLEX_MASK_DOCUMENT || p.kind == FLEX_MASK_DOCUMENT_CAUSAL) {
+        all = r0 + p.q_block <= p.q_len && c_end < p.kv_len;
+        if (doc) {
           // the same classes from the columns' query intervals (p.bounds
           // holds the column bounds here)
           const int r_end = r0 + p.q_block - 1, r_last = r1 - 1;
-          for (int j = c0; j <= c_last; ++j) {
+          for (int j = c0 + sub; j <= c_last; j += kLanes) {
             const int clo = p.bounds[2 * (size_t)j], chi = p.bounds[2 * (size_t)j + 1];
             all = all && clo <= r0 && chi >= r_end;
             any = any || (clo <= chi && clo <= r_last && chi >= r0);
           }
         } else {
-          for (int i = r0; i < r1; ++i) {
+          for (int i = r0 + sub; i < r1; i += kLanes) {
             const RowInterval iv = visible_keys(p, i);
             all = all && iv.lo <= c0 && iv.hi >= c_end;
             any = any || (iv.lo <= iv.hi && iv.lo <= c_last && iv.hi >= c0);
           }
         }
-        c = all ? 2 : (any ? 1 : 0);
       }
+#pragma unroll
+      for (int o = 1; o < kLanes; o <<= 1) {
+        all &= __shfl_xor(all, o);
+        any |= __shfl_xor(any, o);
+      }
+      // one flag per tile, on its first lane: thread order is q-block order
+      const int c = (qb < nq && sub == 0) ? (all ? 2 : (any ? 1 : 0)) : 0;
       int tp, tf;
       const int bp = seen_part + block_prefix(c == 1, scratch, &tp);
       const int bf = seen_full + block_prefix(c == 2, scratch, &tf);
-      if (pass == 1 && qb < nq) {
+      if (pass == 1 && qb < nq && sub == 0) {
         p.kv_idx[col + (c == 1 ? bp : n_part + (qb - bp))] = qb;
         p.fkv_idx[col + (c == 2 ? bf : n_full + (qb - bf))] = qb;
       }
