@@ -361,12 +361,16 @@ struct Bf16BwdDq {
       if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
 #pragma unroll
       for (int b = 0; b < KS / 32; ++b) {
+        // skip a 32-key block no row of the wave sees; mask only one that
+        // some row sees in part
+        bool masked = partial;
         if (partial) {
           const int b0 = kv0 + 32 * b;
           const bool any = lo <= b0 + 31 && hi >= b0 && lo <= hi;
           if (!__any(any)) continue;
+          masked = !__all(lo <= b0 && hi >= b0 + 31);
         }
-        block(cur, b, kv0 + 32 * b + 8 * g, partial);
+        block(cur, b, kv0 + 32 * b + 8 * g, masked);
       }
       s_barrier_full();
     };
@@ -616,12 +620,15 @@ struct Bf16BwdDkv {
       // a listed-full tile at a ragged edge is still handled as partial
       const bool partial = t < np || kv_ragged || qbt * QB + QB > p.q_len;
       if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
-      bool run_it = true;
+      // skip a step no key of the wave is seen by; mask only one that some
+      // key is seen in part by
+      bool run_it = true, masked = partial;
       if (partial) {
         const bool any = qlo <= q00 + QS - 1 && qhi >= q00 && qlo <= qhi;
         run_it = __any(any);
+        masked = !__all(qlo <= q00 && qhi >= q00 + QS - 1);
       }
-      if (run_it) block(cur, q00, partial);
+      if (run_it) block(cur, q00, masked);
       s_barrier_full();
     };
 

@@ -455,13 +455,19 @@ struct Bf16Fwd {
         // On a partial tile, skip a 32-key block that no row of this wave
         // sees: its scores would all be -inf, i.e. weight exactly 0 and no
         // change to the running max.  (Diagonal tiles of a causal mask and
-        // the window edges are mostly such blocks.)
+        // the window edges are mostly such blocks.)  A block that every row
+        // of the wave sees whole needs no mask either.
+        bool masked = partial;
         if (partial) {
           const int b0 = kv0 + 32 * b;
-          bool any = false;
+          bool any = false, all = true;
 #pragma unroll
-          for (int c = 0; c < NQ; ++c) any |= lo[c] <= b0 + 31 && hi[c] >= b0 && lo[c] <= hi[c];
+          for (int c = 0; c < NQ; ++c) {
+            any |= lo[c] <= b0 + 31 && hi[c] >= b0 && lo[c] <= hi[c];
+            all = all && lo[c] <= b0 && hi[c] >= b0 + 31;
+          }
           if (!__any(any)) continue;
+          masked = !__all(all);
         }
         // register r holds key kvl + 16(r >> 3) + (r & 7)
         const int kvl = kv0 + 32 * b + 8 * g;
@@ -486,7 +492,7 @@ struct Bf16Fwd {
           for (int c = 0; c < NQ; ++c) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm[c]);
-            if (partial) mask_block(pv[c], c, kvl, 0.f);
+            if (masked) mask_block(pv[c], c, kvl, 0.f);
             rs[c] = sum16(pv[c]);
             bad |= rs[c] > kPMax;
           }
@@ -509,7 +515,7 @@ struct Bf16Fwd {
           }
 #pragma unroll
           for (int c = 0; c < NQ; ++c) {
-            if (partial) mask_block(s[c], c, kvl, -INFINITY);
+            if (masked) mask_block(s[c], c, kvl, -INFINITY);
             // 16-way max as a v_max3 tree: 8 instructions, depth 3
             const float t0 = max3(s[c][0], s[c][1], s[c][2]);
             const float t1 = max3(s[c][3], s[c][4], s[c][5]);
