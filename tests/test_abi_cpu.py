@@ -163,3 +163,37 @@ def test_bwd_rejects_on_host():
     assert _bwd(lse=None) == fa.FLEX_E_INVALID_ARG             # lse required
     # empty problems succeed without launching anything
     assert _bwd(B=0, ptr=None, ws=None, lse=None) == fa.FLEX_OK
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every ctypes structure of the binding has the size and field offsets
+    the C compiler gives the header's struct (compiled here with gcc)."""
+    import subprocess
+    structs = {
+        "flex_mask_desc": fa.MaskDesc,
+        "flex_block_mask": fa.BlockMaskStruct,
+        "flex_block_mask_t": fa.BlockMaskTStruct,
+        "flex_score_desc": fa.ScoreDesc,
+        "flex_fwd_options": fa.FwdOptions,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "flexattn.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append('  printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for fname, _ in cls._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, fname, cname, fname))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        parts = line.split()
+        if len(parts) == 3:
+            got[(parts[0], parts[1])] = int(parts[2])
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
