@@ -175,9 +175,12 @@ struct Bf16BwdDq {
   static constexpr int STAGE = KS * ROWB;   // bytes of K (or V) per step
   static constexpr int CPR = ROWB / 16;
   static constexpr int NDMA = KS * CPR / (64 * NW);
-  // three waves per SIMD at head dim 64 (128-150 VGPRs); at 128 two, or
-  // one with 64-row tiles (the two-wave work-group's extra load addresses)
-  static constexpr int WAVES_PER_SIMD = (D == 128 && QB == 64) ? 1 : (D == 64 ? 3 : 2);
+  // head dim 64: four waves per SIMD with 128-row tiles (128 VGPRs with 2-3
+  // values spilled; 2-3% faster than three on the prefix and sliding-window
+  // workloads), three with 64-row tiles; head dim 128: two, or one with
+  // 64-row tiles (the two-wave work-group's extra load addresses)
+  static constexpr int WAVES_PER_SIMD =
+      D == 64 ? (QB == 128 ? 4 : 3) : (QB == 64 ? 1 : 2);
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
 
   __device__ static void run(const BwdParams& p) {
@@ -405,9 +408,10 @@ struct Bf16BwdDkv {
   static constexpr int CPR = ROWB / 16;
   static constexpr int NDMA = QS * CPR / (64 * NW);
   // head dim 64: three waves per SIMD (168 VGPRs, with a few spilled; it
-  // measured 4-17% faster than two); head dim 128: the wave's K and V rows
-  // (64 VGPRs) and the dk and dv accumulators (128) leave room for one
-  static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 1;
+  // measured 4-17% faster than two); head dim 128: two (the wave's K and V
+  // rows and the dk and dv accumulators take ~275 registers, ~20 of them
+  // spilled; 13-18% faster than one wave with no spill)
+  static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 2;
   static_assert(NDMA * 64 * NW == QS * CPR, "step split");
 
   __device__ static void run(const BwdParams& p) {
