@@ -13,9 +13,10 @@ oracle on a bounded sample of rows of the same workload.
 `--pass bwd` measures the backward instead: one step = build both block-mask
 arrays (per q-block and per kv-block) on the device, then the backward (the
 per-row delta pass, the dq kernel and the dk/dv kernel) from the forward's
-output and lse, computed once beforehand.  Its `value` counts 10 * D FLOPs per
-visible pair (the five products S, dP, dV, dK, dQ the gradients need, each
-2 * D; the kernels recompute S and dP once more, which is not counted), and
+output and lse, computed once beforehand.  Its `value` counts 6 * D + 4 * Dv
+FLOPs per visible pair (the five products the gradients need: S, dK and dQ
+2 * D each, dP and dV 2 * Dv each; 10 * D with equal head dims; the kernels
+recompute S and dP once more, which is not counted), and
 its `cpu_baseline` times the oracle's backward on whole heads.
 
 `--copy-calibration` instead runs only a plain device-to-device copy of a
@@ -122,7 +123,8 @@ def cpu_baseline_bwd(cfg, q, k, v, dout, target_seconds: float):
     B, H, L, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["d"]
     qf, kf, vf, df = (t.float().numpy() for t in (q, k, v, dout))
     threads = oracle.threads_used()
-    per_head = 10.0 * D * visible_pairs(cfg["mask"], L, cfg["kv_len"])
+    Dv = cfg.get("dv", D)
+    per_head = 2.0 * (3 * D + 2 * Dv) * visible_pairs(cfg["mask"], L, cfg["kv_len"])
     spent, flops, heads_done, h0 = 0.0, 0.0, 0, 0
     while spent < target_seconds and heads_done < B * H:
         n = min(threads, B * H - h0)
@@ -163,6 +165,7 @@ def run_bwd(args, cfg, name, q, k, v):
     dout, _ = make_grad_inputs(cfg)
     dod = dout.to(dev)
     B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
+    Dv = cfg.get("dv", D)
     bargs = (with_doc_ids(cfg, dev), Lq, Lk, cfg["q_block"], cfg["kv_block"])
     bm = fa.build_block_mask(*bargs, device=dev)
     bmt = fa.build_block_mask_t(*bargs, device=dev)
@@ -170,7 +173,7 @@ def run_bwd(args, cfg, name, q, k, v):
     gd = qd.dtype
     dq = torch.empty((B, H, Lq, D), dtype=gd, device=dev)
     dk = torch.empty((B, H, Lk, D), dtype=gd, device=dev)
-    dv = torch.empty((B, H, Lk, D), dtype=gd, device=dev)
+    dv = torch.empty((B, H, Lk, Dv), dtype=gd, device=dev)
     ws = torch.empty(max(fa.bwd_workspace_floats(B, H, Lq), 1), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -199,7 +202,7 @@ def run_bwd(args, cfg, name, q, k, v):
     bwd_ms = [a.elapsed_time(b) for a, b in events]
     bwd_avg_ms = float(np.mean(bwd_ms))
     pairs = visible_pairs(cfg["mask"], Lq, Lk)
-    flops = 10.0 * B * H * D * pairs
+    flops = 2.0 * B * H * (3 * D + 2 * Dv) * pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (bwd_avg_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS
@@ -218,7 +221,7 @@ def run_bwd(args, cfg, name, q, k, v):
         "data": "synthetic",
         "config": {
             "workload": name, "B": B, "H": H, "q_len": Lq, "kv_len": Lk, "head_dim": D,
-            "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
+            "v_head_dim": Dv, "q_block": cfg["q_block"], "kv_block": cfg["kv_block"],
             "mask": _printable_mask(cfg["mask"]),
             "score_mod": cfg["score"]["kind"], "grad_dtype": cfg["dtype"],
             "visible_pairs_per_head": pairs,

@@ -266,12 +266,12 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
 int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, const float* dlse,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
-                      int32_t kv_len, int32_t head_dim, const flex_block_mask* bm,
-                      const flex_block_mask_t* bmt, const flex_score_desc* score,
-                      float scale, void* dq, void* dk, void* dv, int32_t grad_dtype,
-                      float* workspace, void* stream) {
+                      int32_t kv_len, int32_t head_dim, int32_t v_head_dim,
+                      const flex_block_mask* bm, const flex_block_mask_t* bmt,
+                      const flex_score_desc* score, float scale, void* dq, void* dk,
+                      void* dv, int32_t grad_dtype, float* workspace, void* stream) {
   if (!bm || !bmt) return FLEX_E_INVALID_ARG;
-  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0)
+  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0 || head_dim <= 0 || v_head_dim <= 0)
     return FLEX_E_INVALID_ARG;
   if (in_dtype != FLEX_DTYPE_BF16 && in_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
   if (grad_dtype != FLEX_DTYPE_BF16 && grad_dtype != FLEX_DTYPE_FP32) return FLEX_E_INVALID_ARG;
@@ -297,13 +297,14 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
       bias_max = score->bias_max;
     }
   }
-  if (!bwd_supported(in_dtype, head_dim, bm->q_block, bm->kv_block))
+  if (!bwd_supported(in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block))
     return FLEX_E_UNSUPPORTED;
 
   const int64_t rows = (int64_t)B * H * q_len;
   const int64_t krows = (int64_t)B * H * kv_len;
   if ((int64_t)B * H * bm->n_q_blocks > INT32_MAX || (int64_t)B * H * bm->n_kv_blocks > INT32_MAX ||
-      rows * head_dim > ((int64_t)1 << 40) || krows * head_dim > ((int64_t)1 << 40))
+      rows * head_dim > ((int64_t)1 << 40) || krows * head_dim > ((int64_t)1 << 40) ||
+      rows * v_head_dim > ((int64_t)1 << 40) || krows * v_head_dim > ((int64_t)1 << 40))
     return FLEX_E_INVALID_ARG;
   if (rows == 0 && krows == 0) return FLEX_OK;  // nothing to write
   if (rows > 0 && (!q || !out || !dout || !lse || !dq || !workspace)) return FLEX_E_INVALID_ARG;
@@ -360,8 +361,8 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   p.neg = scale < 0.f ? 1 : 0;
   p.bias_max = bias_max;
   p.grad_bf16 = grad_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
-  return launch_bwd(p, head_dim, bm->q_block, bm->kv_block, bm->mask.kind, score_kind,
-                    static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_bwd(p, head_dim, v_head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
+                    score_kind, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
 }

@@ -133,20 +133,21 @@ __device__ inline void pack16(const float (&x)[16], bf16x8 (&pk)[2]) {
 }
 
 // ---------------------------------------------------------------------------
-// Per query row: ws[row] = -delta, ws[rows + row] = a.  D / 8 lanes per row,
-// each reading 8 elements of out and dout.
+// Per query row: ws[row] = -delta, ws[rows + row] = a.  DV / 8 lanes per row
+// (DV the value head dim, the width of out and dout), each reading 8
+// elements of out and dout.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int DV>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
+  constexpr int LPR = DV / 8;
   const long long rows = (long long)p.B * p.H * p.q_len;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = t / LPR;
   const int part = (int)(t % LPR);
   float acc = 0.f;
   if (row < rows) {
-    const u32x4 o = ld_global16(static_cast<const char*>(p.out) + (row * D + part * 8) * 2);
-    const u32x4 d = ld_global16(static_cast<const char*>(p.dout) + (row * D + part * 8) * 2);
+    const u32x4 o = ld_global16(static_cast<const char*>(p.out) + (row * DV + part * 8) * 2);
+    const u32x4 d = ld_global16(static_cast<const char*>(p.dout) + (row * DV + part * 8) * 2);
     const bf16x8 ob = __builtin_bit_cast(bf16x8, o), db = __builtin_bit_cast(bf16x8, d);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf((float)ob[i], (float)db[i], acc);
@@ -164,28 +165,35 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dq
 // ---------------------------------------------------------------------------
-template <int D, int QB, int KB, int MASK, int SCORE>
+// D: head dim of q and k; DV: value head dim (width of v, out and dout)
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 struct Bf16BwdDq {
   static constexpr int NW = QB / 32;
   static constexpr int NT = 64 * NW;
   static constexpr int KS = 64;             // keys per step
   static constexpr int SPT = KB / KS;
   static constexpr int NE = D / 32;
-  static constexpr int ROWB = D * 2;
-  static constexpr int STAGE = KS * ROWB;   // bytes of K (or V) per step
+  static constexpr int ROWB = D * 2;        // bytes per K row
+  static constexpr int ROWBV = DV * 2;      // bytes per V row
+  static constexpr int STAGE = KS * ROWB;   // bytes of K per step (V follows)
+  static constexpr int STAGEV = KS * ROWBV; // bytes of V per step
   static constexpr int CPR = ROWB / 16;
+  static constexpr int CPRV = ROWBV / 16;
   static constexpr int NDMA = KS * CPR / (64 * NW);
+  static constexpr int NDMAV = KS * CPRV / (64 * NW);
   // head dim 64: four waves per SIMD with 128-row tiles (128 VGPRs with 2-3
   // values spilled; 2-3% faster than three on the prefix and sliding-window
-  // workloads), three with 64-row tiles; head dim 128: two, or one with
-  // 64-row tiles (the two-wave work-group's extra load addresses)
+  // workloads), three with 64-row tiles, one fewer each when the dout rows
+  // are 128 wide; head dim 128: two, or one with 64-row tiles (the two-wave
+  // work-group's extra load addresses)
   static constexpr int WAVES_PER_SIMD =
-      D == 64 ? (QB == 128 ? 4 : 3) : (QB == 64 ? 1 : 2);
+      D == 64 ? (QB == 128 ? 4 : 3) - (DV == 64 ? 0 : 1) : (QB == 64 ? 1 : 2);
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
+  static_assert(NDMAV * 64 * NW == KS * CPRV, "step split (V)");
 
   __device__ static void run(const BwdParams& p) {
-    __shared__ __attribute__((aligned(16))) char sb0[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) char sb1[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char sb0[STAGE + STAGEV];
+    __shared__ __attribute__((aligned(16))) char sb1[STAGE + STAGEV];
     lds_t* const buf[2] = {(lds_t*)sb0, (lds_t*)sb1};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -200,16 +208,20 @@ struct Bf16BwdDq {
     const long long rows = (long long)p.B * p.H * p.q_len;
     const size_t head_q = (size_t)bh * p.q_len;
     const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
-    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWB;
+    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWBV;
     const char* kg = static_cast<const char*>(p.k) + (size_t)bh * p.kv_len * ROWB;
-    const char* vg = static_cast<const char*>(p.v) + (size_t)bh * p.kv_len * ROWB;
+    const char* vg = static_cast<const char*>(p.v) + (size_t)bh * p.kv_len * ROWBV;
 
     // A-operand row reads: row swap23(lq), 16-byte piece 2t + g in V layout
+    // (K rows D wide, V rows DV wide)
     const int ra = swap23(lq);
-    int kra[D / 16];
+    int kra[D / 16], vra[DV / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
       kra[t] = ra * ROWB + (((2 * t + g) ^ (vswz<D>(ra) >> 1)) << 4);
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t)
+      vra[t] = ra * ROWBV + (((2 * t + g) ^ (vswz<DV>(ra) >> 1)) << 4);
     // transposing reads (the forward's V^T fragment offsets)
     int tro[NE];
     {
@@ -222,13 +234,15 @@ struct Bf16BwdDq {
     // q and dout fragments (B operands), one query row per lane
     const int qi = q0 + wave * 32 + lq;
     const bool ok = qi < p.q_len;
-    u32x4 qf[D / 16], dof[D / 16];
+    u32x4 qf[D / 16], dof[DV / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       qf[t] = ok ? ld_global16(qg + (size_t)qi * ROWB + (2 * t + g) * 16) : u32x4{0, 0, 0, 0};
-      dof[t] = ok ? ld_global16(dog + (size_t)qi * ROWB + (2 * t + g) * 16) : u32x4{0, 0, 0, 0};
       if (p.neg) qf[t] ^= 0x80008000u;
     }
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t)
+      dof[t] = ok ? ld_global16(dog + (size_t)qi * ROWBV + (2 * t + g) * 16) : u32x4{0, 0, 0, 0};
     const long long row = (long long)head_q + min(qi, max(p.q_len - 1, 0));
     const float ndelta = ok ? p.ws[row] : 0.f;
     const float nm = ok ? p.c1 * p.ws[rows + row] : -INFINITY;  // c1 a (-inf: no key)
@@ -270,15 +284,23 @@ struct Bf16BwdDq {
       const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
       const int rows_left = min(KS, p.kv_len - kv0);
       const char* kt = kg + (size_t)kv0 * ROWB;
-      const char* vt = vg + (size_t)kv0 * ROWB;
+      const char* vt = vg + (size_t)kv0 * ROWBV;
 #pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int sl = (wave * NDMA + j) * 64 + lane;
-        const int r = sl / CPR, q = sl % CPR;
-        const int rr = min(r, rows_left - 1);
-        const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
-        __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMA + j) * 1024), 16, 0, 0);
+      for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
+        if (j < NDMA) {
+          const int sl = (wave * NDMA + j) * 64 + lane;
+          const int r = sl / CPR, q = sl % CPR;
+          const int rr = min(r, rows_left - 1);
+          const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+          __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
+        }
+        if (j < NDMAV) {
+          const int sl = (wave * NDMAV + j) * 64 + lane;
+          const int r = sl / CPRV, q = sl % CPRV;
+          const int rr = min(r, rows_left - 1);
+          const unsigned off = (unsigned)(rr * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
+          __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMAV + j) * 1024), 16, 0, 0);
+        }
       }
     };
 
@@ -304,16 +326,19 @@ struct Bf16BwdDq {
         s = f32x16{};
       }
       f32x16 dp = f32x16{};
-      bf16x8 kf[D / 16], vf[D / 16];
+      bf16x8 kf[D / 16], vf[DV / 16];
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
+      for (int t = 0; t < D / 16; ++t)
         kf[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + kra[t] + 32 * b * ROWB));
-        vf[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + STAGE + kra[t] + 32 * b * ROWB));
-      }
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], __builtin_bit_cast(bf16x8, qf[t]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], __builtin_bit_cast(bf16x8, dof[t]), dp, 0, 0, 0);
+      for (int t = 0; t < DV / 16; ++t)
+        vf[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + STAGE + vra[t] + 32 * b * ROWBV));
+#pragma unroll
+      for (int t = 0; t < (D > DV ? D : DV) / 16; ++t) {
+        if (t < D / 16)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], __builtin_bit_cast(bf16x8, qf[t]), s, 0, 0, 0);
+        if (t < DV / 16)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], __builtin_bit_cast(bf16x8, dof[t]), dp, 0, 0, 0);
       }
       // K^T fragments for dq^T += K^T ds^T
       bf16x8 ktf[NE][2];
@@ -394,25 +419,31 @@ struct Bf16BwdDq {
 // ---------------------------------------------------------------------------
 // dk, dv
 // ---------------------------------------------------------------------------
-template <int D, int QB, int KB, int MASK, int SCORE>
+// D: head dim of q and k; DV: value head dim (width of v, out and dout)
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 struct Bf16BwdDkv {
   static constexpr int NW = KB / 32;        // one wave per 32 keys
   static constexpr int NT = 64 * NW;
   static constexpr int QS = 32;             // query rows per step
   static constexpr int SPQ = QB / QS;       // steps per listed q-block
-  static constexpr int NE = D / 32;
-  static constexpr int ROWB = D * 2;
-  static constexpr int TILE = QS * ROWB;    // bytes of q (or dout) per step
-  static constexpr int ARR = TILE * 2;      // offset of the per-row arrays
+  static constexpr int NE = D / 32;         // dk accumulators
+  static constexpr int NEV = DV / 32;       // dv accumulators
+  static constexpr int ROWB = D * 2;        // bytes per q row
+  static constexpr int ROWBV = DV * 2;      // bytes per dout row
+  static constexpr int TILE = QS * ROWB;    // bytes of q per step (dout follows)
+  static constexpr int ARR = TILE + QS * ROWBV;  // offset of the per-row arrays
   static constexpr int STAGEB = ARR + 2 * QS * 4;
   static constexpr int CPR = ROWB / 16;
+  static constexpr int CPRV = ROWBV / 16;
   static constexpr int NDMA = QS * CPR / (64 * NW);
-  // head dim 64: three waves per SIMD (168 VGPRs, with a few spilled; it
-  // measured 4-17% faster than two); head dim 128: two (the wave's K and V
-  // rows and the dk and dv accumulators take ~275 registers, ~20 of them
-  // spilled; 13-18% faster than one wave with no spill)
-  static constexpr int WAVES_PER_SIMD = D == 64 ? 3 : 2;
+  static constexpr int NDMAV = QS * CPRV / (64 * NW);
+  // head dims 64/64: three waves per SIMD (168 VGPRs, with a few spilled; it
+  // measured 4-17% faster than two); 128/128: two (the wave's K and V rows
+  // and the dk and dv accumulators take ~275 registers, ~20 of them spilled;
+  // 13-18% faster than one wave with no spill); 64/128 and 128/64: two
+  static constexpr int WAVES_PER_SIMD = D == 64 && DV == 64 ? 3 : 2;
   static_assert(NDMA * 64 * NW == QS * CPR, "step split");
+  static_assert(NDMAV * 64 * NW == QS * CPRV, "step split (dout)");
 
   __device__ static void run(const BwdParams& p) {
     __shared__ __attribute__((aligned(16))) char sb0[STAGEB];
@@ -434,23 +465,24 @@ struct Bf16BwdDkv {
     const size_t head_q = (size_t)bh * p.q_len;
     const size_t head_kv = (size_t)bh * p.kv_len;
     const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
-    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWB;
+    const char* dog = static_cast<const char*>(p.dout) + head_q * ROWBV;
     const bool kv_ragged = kb * KB + KB > p.kv_len;
 
     // this lane's key, its K and V rows (B operands), its visible queries
     const int kk = kb * KB + wave * 32 + lq;
     const bool kok = kk < p.kv_len;
     const int kcl = min(kk, p.kv_len - 1);
-    u32x4 kf[D / 16], vf[D / 16];
+    u32x4 kf[D / 16], vf[DV / 16];
     {
       const char* kr = static_cast<const char*>(p.k) + (head_kv + kcl) * ROWB;
-      const char* vr = static_cast<const char*>(p.v) + (head_kv + kcl) * ROWB;
+      const char* vr = static_cast<const char*>(p.v) + (head_kv + kcl) * ROWBV;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         kf[t] = ld_global16(kr + (2 * t + g) * 16);
-        vf[t] = ld_global16(vr + (2 * t + g) * 16);
         if (p.neg) kf[t] ^= 0x80008000u;
       }
+#pragma unroll
+      for (int t = 0; t < DV / 16; ++t) vf[t] = ld_global16(vr + (2 * t + g) * 16);
     }
     int qlo, qhi;
     col_interval<MASK>(p, kk, qlo, qhi);
@@ -462,16 +494,23 @@ struct Bf16BwdDkv {
     }
 
     // A-operand row reads of the q / dout tiles, and transposing reads
+    // (q rows D wide, dout rows DV wide)
     const int ra = swap23(lq);
-    int qra[D / 16];
+    int qra[D / 16], dra[DV / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) qra[t] = ra * ROWB + (((2 * t + g) ^ (vswz<D>(ra) >> 1)) << 4);
-    int tro[NE];
+#pragma unroll
+    for (int t = 0; t < DV / 16; ++t)
+      dra[t] = ra * ROWBV + (((2 * t + g) ^ (vswz<DV>(ra) >> 1)) << 4);
+    int tro[NE], trov[NEV];
     {
       const int j = lane & 15, u = (lane >> 4) & 1;
       const int r0 = 8 * g + (j >> 2);
 #pragma unroll
       for (int e = 0; e < NE; ++e) tro[e] = r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz<D>(r0)) << 3);
+#pragma unroll
+      for (int e = 0; e < NEV; ++e)
+        trov[e] = r0 * ROWBV + (((8 * e + 4 * u + (j & 3)) ^ vswz<DV>(r0)) << 3);
     }
 
     // transposed tile list of this kv-block
@@ -504,15 +543,23 @@ struct Bf16BwdDkv {
       const int r00 = min(qbm * QB + (m % SPQ) * QS, p.q_len - 1);
       const int rows_left = min(QS, p.q_len - r00);
       const char* qt = qg + (size_t)r00 * ROWB;
-      const char* dt = dog + (size_t)r00 * ROWB;
+      const char* dt = dog + (size_t)r00 * ROWBV;
 #pragma unroll
-      for (int j = 0; j < NDMA; ++j) {
-        const int sl = (wave * NDMA + j) * 64 + lane;
-        const int r = sl / CPR, q = sl % CPR;
-        const int rr = min(r, rows_left - 1);
-        const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
-        __builtin_amdgcn_global_load_lds(qt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(dt + off, (__attribute__((address_space(3))) void*)(dst + TILE + (wave * NDMA + j) * 1024), 16, 0, 0);
+      for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
+        if (j < NDMA) {
+          const int sl = (wave * NDMA + j) * 64 + lane;
+          const int r = sl / CPR, q = sl % CPR;
+          const int rr = min(r, rows_left - 1);
+          const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+          __builtin_amdgcn_global_load_lds(qt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
+        }
+        if (j < NDMAV) {
+          const int sl = (wave * NDMAV + j) * 64 + lane;
+          const int r = sl / CPRV, q = sl % CPRV;
+          const int rr = min(r, rows_left - 1);
+          const unsigned off = (unsigned)(rr * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
+          __builtin_amdgcn_global_load_lds(dt + off, (__attribute__((address_space(3))) void*)(dst + TILE + (wave * NDMAV + j) * 1024), 16, 0, 0);
+        }
       }
       if (wave == 0) {
         const int r = min(lq, rows_left - 1);
@@ -522,12 +569,11 @@ struct Bf16BwdDkv {
       }
     };
 
-    f32x16 dk[NE], dv[NE];
+    f32x16 dk[NE], dv[NEV];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      dk[e] = f32x16{};
-      dv[e] = f32x16{};
-    }
+    for (int e = 0; e < NE; ++e) dk[e] = f32x16{};
+#pragma unroll
+    for (int e = 0; e < NEV; ++e) dv[e] = f32x16{};
 
     // one step: 32 query rows q00.. against this wave's 32 keys
     auto block = [&](const lds_t* cur, int q00, bool partial) {
@@ -560,30 +606,37 @@ struct Bf16BwdDkv {
           y += bias_u;
         }
       }
-      bf16x8 qa[D / 16], da[D / 16];
+      bf16x8 qa[D / 16], da[DV / 16];
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        qa[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + qra[t]));
-        da[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + TILE + qra[t]));
-      }
+      for (int t = 0; t < D / 16; ++t) qa[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + qra[t]));
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, kf[t]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], __builtin_bit_cast(bf16x8, vf[t]), dp, 0, 0, 0);
+      for (int t = 0; t < DV / 16; ++t)
+        da[t] = __builtin_bit_cast(bf16x8, FLEXATTN_LDS(u32x4, cur + TILE + dra[t]));
+#pragma unroll
+      for (int t = 0; t < (D > DV ? D : DV) / 16; ++t) {
+        if (t < D / 16)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], __builtin_bit_cast(bf16x8, kf[t]), s, 0, 0, 0);
+        if (t < DV / 16)
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], __builtin_bit_cast(bf16x8, vf[t]), dp, 0, 0, 0);
       }
       // transposed fragments of dout and q for the two accumulations
-      bf16x8 dot[NE][2], qt[NE][2];
+      bf16x8 dot[NEV][2], qt[NE][2];
+#pragma unroll
+      for (int e = 0; e < NEV; ++e)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const lds_t* dp0 = cur + TILE + trov[e] + 16 * hh * ROWBV;
+          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)dp0);
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(dp0 + 4 * ROWBV));
+          dot[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
 #pragma unroll
       for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const lds_t* dp0 = cur + TILE + tro[e] + 16 * hh * ROWB;
           const lds_t* qp0 = cur + tro[e] + 16 * hh * ROWB;
-          const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)dp0);
-          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(dp0 + 4 * ROWB));
           const i16x4 q0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)qp0);
           const i16x4 q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(qp0 + 4 * ROWB));
-          dot[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
           qt[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       // p = 2^(c1 s), masked on partial tiles; ds = p dP
@@ -603,11 +656,11 @@ struct Bf16BwdDkv {
       pack16(pv, pp);
       pack16(ds, pd);
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
+      for (int e = 0; e < (NE > NEV ? NE : NEV); ++e)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot[e][hh], pp[hh], dv[e], 0, 0, 0);
-          dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[e][hh], pd[hh], dk[e], 0, 0, 0);
+          if (e < NEV) dv[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot[e][hh], pp[hh], dv[e], 0, 0, 0);
+          if (e < NE) dk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[e][hh], pd[hh], dk[e], 0, 0, 0);
         }
     };
 
@@ -648,81 +701,81 @@ struct Bf16BwdDkv {
 
     if (kok) {
       write_row_t<NE>(p.dk, p.grad_bf16 != 0, head_kv + kk, D, g, dk, p.scale);
-      write_row_t<NE>(p.dv, p.grad_bf16 != 0, head_kv + kk, D, g, dv, 1.0f);
+      write_row_t<NEV>(p.dv, p.grad_bf16 != 0, head_kv + kk, DV, g, dv, 1.0f);
     }
   }
 };
 
 #undef FLEXATTN_LDS
 
-template <int D, int QB, int KB, int MASK, int SCORE>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDq<D, QB, KB, MASK, SCORE>::NT),
-                          amdgpu_waves_per_eu(Bf16BwdDq<D, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDq<D, DV, QB, KB, MASK, SCORE>::NT),
+                          amdgpu_waves_per_eu(Bf16BwdDq<D, DV, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
 void bwd_dq_kernel(BwdParams p) {
-  Bf16BwdDq<D, QB, KB, MASK, SCORE>::run(p);
+  Bf16BwdDq<D, DV, QB, KB, MASK, SCORE>::run(p);
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDkv<D, QB, KB, MASK, SCORE>::NT),
-                          amdgpu_waves_per_eu(Bf16BwdDkv<D, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Bf16BwdDkv<D, DV, QB, KB, MASK, SCORE>::NT),
+                          amdgpu_waves_per_eu(Bf16BwdDkv<D, DV, QB, KB, MASK, SCORE>::WAVES_PER_SIMD)))
 void bwd_dkv_kernel(BwdParams p) {
-  Bf16BwdDkv<D, QB, KB, MASK, SCORE>::run(p);
+  Bf16BwdDkv<D, DV, QB, KB, MASK, SCORE>::run(p);
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
   const long long rows = (long long)p.B * p.H * p.q_len;
   if (rows > 0) {
-    const long long threads = rows * (D / 8);
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    const long long threads = rows * (DV / 8);
+    hipLaunchKernelGGL(bwd_pre_kernel<DV>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long long nq = (long long)p.B * p.H * p.n_qb;
   if (nq > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
-                       dim3(Bf16BwdDq<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
+                       dim3(Bf16BwdDq<D, DV, QB, KB, MASK, SCORE>::NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long long nkv = (long long)p.B * p.H * p.n_kb;
   if (nkv > 0) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nkv),
-                       dim3(Bf16BwdDkv<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nkv),
+                       dim3(Bf16BwdDkv<D, DV, QB, KB, MASK, SCORE>::NT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <int D, int QB, int KB, int MASK>
+template <int D, int DV, int QB, int KB, int MASK>
 hipError_t bwd_pick_score(const BwdParams& p, int score, hipStream_t s) {
-  if (score == FLEX_SCORE_REL_BIAS) return launch_bwd_one<D, QB, KB, MASK, FLEX_SCORE_REL_BIAS>(p, s);
-  return launch_bwd_one<D, QB, KB, MASK, FLEX_SCORE_IDENTITY>(p, s);
+  if (score == FLEX_SCORE_REL_BIAS) return launch_bwd_one<D, DV, QB, KB, MASK, FLEX_SCORE_REL_BIAS>(p, s);
+  return launch_bwd_one<D, DV, QB, KB, MASK, FLEX_SCORE_IDENTITY>(p, s);
 }
 
-template <int D, int QB, int KB>
+template <int D, int DV, int QB, int KB>
 hipError_t bwd_pick_mask(const BwdParams& p, int mask, int score, hipStream_t s) {
   switch (mask) {
     case FLEX_MASK_NOOP:
-      return bwd_pick_score<D, QB, KB, FLEX_MASK_NOOP>(p, score, s);
+      return bwd_pick_score<D, DV, QB, KB, FLEX_MASK_NOOP>(p, score, s);
     case FLEX_MASK_CAUSAL:
-      return bwd_pick_score<D, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
+      return bwd_pick_score<D, DV, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
     case FLEX_MASK_SLIDING_WINDOW:
-      return bwd_pick_score<D, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
+      return bwd_pick_score<D, DV, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
     case FLEX_MASK_DOCUMENT:
     case FLEX_MASK_DOCUMENT_CAUSAL:
-      return bwd_pick_score<D, QB, KB, FLEX_MASK_DOCUMENT>(p, score, s);
+      return bwd_pick_score<D, DV, QB, KB, FLEX_MASK_DOCUMENT>(p, score, s);
     default:
-      return bwd_pick_score<D, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
+      return bwd_pick_score<D, DV, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
   }
 }
 
 }  // namespace bwd
 }  // namespace flexattn
 
-#define FLEXATTN_BWD_UNIT(NAME, D, QB, KB)                                         \
+#define FLEXATTN_BWD_UNIT(NAME, D, DV, QB, KB)                                     \
   namespace flexattn {                                                           \
   hipError_t NAME(const BwdParams& p, int mask, int score, hipStream_t s) {      \
-    return bwd::bwd_pick_mask<D, QB, KB>(p, mask, score, s);                     \
+    return bwd::bwd_pick_mask<D, DV, QB, KB>(p, mask, score, s);                 \
   }                                                                              \
   }

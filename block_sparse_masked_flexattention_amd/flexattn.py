@@ -23,7 +23,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -119,7 +119,7 @@ def load(path: str | None = None):
                                                        ctypes.POINTER(ctypes.c_int64)]
         lib.flex_attn_bwd_workspace_floats.restype = i32
         lib.flex_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
-                                      ctypes.POINTER(BlockMaskStruct),
+                                      i32, ctypes.POINTER(BlockMaskStruct),
                                       ctypes.POINTER(BlockMaskTStruct),
                                       ctypes.POINTER(ScoreDesc), ctypes.c_float, vp, vp, vp,
                                       i32, vp, vp]
@@ -361,13 +361,15 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
         dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
     """Gradients (dq, dk, dv) of the masked attention forward.  q/k/v/out/dout
-    as in ``fwd`` (out and lse the forward's results), lse float32 [B,H,Lq]."""
+    as in ``fwd`` (out and lse the forward's results), lse float32 [B,H,Lq].
+    v, out, dout and dv may have a value head dim Dv other than q's D."""
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
-    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, D):
+    Dv = v.shape[3] if v.dim() == 4 else -1
+    if k.shape != (B, H, Lk, D) or v.shape != (B, H, Lk, Dv):
         raise ValueError("q/k/v shapes disagree")
-    if out.shape != (B, H, Lq, D) or dout.shape != (B, H, Lq, D):
-        raise ValueError("out/dout shapes disagree with q")
+    if out.shape != (B, H, Lq, Dv) or dout.shape != (B, H, Lq, Dv):
+        raise ValueError("out/dout shapes disagree with q and v")
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, out, dout)):
         raise ValueError("q/k/v/out/dout must share a dtype in {bfloat16, float32}")
     for t in (q, k, v, out, dout):
@@ -381,12 +383,12 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     gd = grad_dtype or torch.float32
     if gd not in _DT:
         raise ValueError("grad_dtype must be bfloat16 or float32")
-    mk = lambda L: torch.empty((B, H, L, D), dtype=gd, device=q.device)
-    dq = mk(Lq) if dq is None else dq
-    dk = mk(Lk) if dk is None else dk
-    dv = mk(Lk) if dv is None else dv
-    for t, L in ((dq, Lq), (dk, Lk), (dv, Lk)):
-        if t.shape != (B, H, L, D) or t.dtype != gd or not t.is_contiguous():
+    mk = lambda L, d: torch.empty((B, H, L, d), dtype=gd, device=q.device)
+    dq = mk(Lq, D) if dq is None else dq
+    dk = mk(Lk, D) if dk is None else dk
+    dv = mk(Lk, Dv) if dv is None else dv
+    for t, L, d in ((dq, Lq, D), (dk, Lk, D), (dv, Lk, Dv)):
+        if t.shape != (B, H, L, d) or t.dtype != gd or not t.is_contiguous():
             raise ValueError("bad gradient tensor")
     nws = bwd_workspace_floats(B, H, Lq)
     if workspace is None:
@@ -402,7 +404,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     _check(load().flex_attn_bwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), dlse.data_ptr() if dlse is not None else None, _DT[q.dtype],
-        B, H, Lq, Lk, D, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
+        B, H, Lq, Lk, D, Dv, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _DT[gd], workspace.data_ptr(),
         _stream_handle(q.device)), "flex_attn_bwd")
     return dq, dk, dv

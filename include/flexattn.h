@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 4
+#define FLEXATTN_ABI_VERSION 5
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -273,7 +273,8 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
  *   ds_ij = p_ij (<dout_i, v_j> - delta_i),
  *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
  *   dv_j = sum_i p_ij dout_i.
- *   q, out, dout [B, H, q_len, head_dim], k, v [B, H, kv_len, head_dim]:
+ *   q [B, H, q_len, head_dim], k [B, H, kv_len, head_dim],
+ *   v [B, H, kv_len, v_head_dim], out, dout [B, H, q_len, v_head_dim]:
  *   contiguous, element type in_dtype, 16-byte aligned device pointers; out
  *   and lse must be the forward's results for these inputs, mask and score.
  *   lse: fp32 [B, H, q_len] (natural log; -inf for a row that sees no key).
@@ -281,22 +282,23 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
  *   bm: the forward's block mask; bmt: its transpose (same mask and block
  *   sizes), both host pointers to structs of device arrays.
  *   score, scale: as in the forward call.
- *   dq [B, H, q_len, head_dim], dk, dv [B, H, kv_len, head_dim] of grad_dtype
- *   (BF16 or FP32), 16-byte aligned, written in full (zero where nothing
- *   contributes).
+ *   dq [B, H, q_len, head_dim], dk [B, H, kv_len, head_dim],
+ *   dv [B, H, kv_len, v_head_dim] of grad_dtype (BF16 or FP32), 16-byte
+ *   aligned, written in full (zero where nothing contributes).
  *   workspace: device fp32, flex_attn_bwd_workspace_floats() floats, owned by
  *   the caller; its contents on entry are ignored and left undefined.
- * Built instances: in_dtype BF16, head_dim 64 or 128, (q_block, kv_block) in
- * {(64, 64), (128, 64), (128, 128)}, any mask kind and score kind.
+ * Built instances: in_dtype BF16, head_dim and v_head_dim each 64 or 128,
+ * (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}, any mask kind and
+ * score kind.
  * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED (other instances, scale 0
  * or not finite), FLEX_E_HIP. */
 int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                       const void* dout, const float* lse, const float* dlse,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
-                      int32_t kv_len, int32_t head_dim, const flex_block_mask* bm,
-                      const flex_block_mask_t* bmt, const flex_score_desc* score,
-                      float scale, void* dq, void* dk, void* dv, int32_t grad_dtype,
-                      float* workspace, void* stream);
+                      int32_t kv_len, int32_t head_dim, int32_t v_head_dim,
+                      const flex_block_mask* bm, const flex_block_mask_t* bmt,
+                      const flex_score_desc* score, float scale, void* dq, void* dk,
+                      void* dv, int32_t grad_dtype, float* workspace, void* stream);
 
 #ifdef __cplusplus
 }

@@ -128,7 +128,7 @@ def test_fwd_rejects_on_host():
     assert _fwd(Lq=0, ptr=None) == fa.FLEX_OK
 
 
-def _bwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
+def _bwd(B=1, H=1, Lq=128, Lk=128, D=64, Dv=None, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask=None,
          score=None, scale=0.125, grad_dtype=fa.DTYPE_FP32, ptr=0x1000, ws=0x1000,
          t_blocks=None, lse=0x1000):
     mask = mask or {"kind": "causal"}
@@ -138,7 +138,7 @@ def _bwd(B=1, H=1, Lq=128, Lk=128, D=64, dtype=fa.DTYPE_BF16, qb=64, kb=64, mask
     bmt = fa.BlockMaskTStruct(tq, tk, nq, nk, ptr, ptr, ptr, ptr)
     sd = None if score is None else ctypes.byref(score)
     return fa.load().flex_attn_bwd(ptr, ptr, ptr, ptr, ptr, lse, None, dtype, B, H, Lq, Lk, D,
-                                   ctypes.byref(bm), ctypes.byref(bmt), sd, scale,
+                                   D if Dv is None else Dv, ctypes.byref(bm), ctypes.byref(bmt), sd, scale,
                                    ptr, ptr, ptr, grad_dtype, ws, None)
 
 
@@ -153,6 +153,8 @@ def test_bwd_rejects_on_host():
     assert _bwd(grad_dtype=7) == fa.FLEX_E_INVALID_ARG
     assert _bwd(t_blocks=(128, 64)) == fa.FLEX_E_INVALID_ARG    # transposed mask of other blocks
     assert _bwd(D=96) == fa.FLEX_E_UNSUPPORTED                 # head dims 64 and 128 only
+    assert _bwd(Dv=96) == fa.FLEX_E_UNSUPPORTED
+    assert _bwd(Dv=0) == fa.FLEX_E_INVALID_ARG
     assert _bwd(dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # bf16 inputs only
     assert _bwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED

@@ -202,6 +202,40 @@ def test_fully_masked_rows_and_keys():
     check((dq, dk, dv), ref, torch.float32, "fully masked")
 
 
+# value head dim Dv other than the query / key head dim D (v, out, dout and
+# dv are Dv wide): both orders, every tile shape, ragged tails
+DV_CASES = [
+    ("prefix_causal", dict(B=1, H=2, q_len=777, kv_len=777, d=64, dv=128,
+                           mask={"kind": "prefix_causal", "prefix": 300})),
+    ("prefix_causal", dict(B=1, H=1, q_len=333, kv_len=333, d=64, dv=128, q_block=64, kv_block=64,
+                           mask={"kind": "causal"})),
+    ("prefix_causal", dict(B=1, H=1, q_len=520, kv_len=520, d=64, dv=128, q_block=128,
+                           kv_block=128, mask={"kind": "sliding_window", "window": 150,
+                                               "window_min": 2})),
+    ("prefix_causal", dict(B=1, H=2, q_len=600, kv_len=600, d=128, dv=64,
+                           mask={"kind": "causal"})),
+    ("prefix_causal", dict(B=1, H=1, q_len=300, kv_len=650, d=128, dv=64, q_block=64,
+                           kv_block=64, mask={"kind": "noop"})),
+    ("prefix_causal", dict(B=1, H=1, q_len=450, kv_len=450, d=128, dv=64, q_block=128,
+                           kv_block=128, mask={"kind": "prefix_causal", "prefix": 100})),
+    ("causal_rel_bias", dict(B=1, H=4, q_len=260, kv_len=260, d=64, dv=128)),
+    ("causal_rel_bias", dict(B=1, H=4, q_len=260, kv_len=260, d=128, dv=64, q_block=128,
+                             kv_block=64)),
+]
+
+
+@pytest.mark.parametrize("name,over", DV_CASES,
+                         ids=[f"{n}-{o['d']}-{o['dv']}-{i}" for i, (n, o) in enumerate(DV_CASES)])
+def test_value_head_dim_parity(name, over):
+    _case(name, over)
+
+
+@pytest.mark.parametrize("i", [0, 3])
+def test_value_head_dim_bf16_grads_and_lse_gradient(i):
+    name, over = DV_CASES[i]
+    _case(name, over, grad_dtype=torch.bfloat16, with_dlse=True)
+
+
 # ---- full-size workloads in the benchmark's launch configuration; the oracle
 # computes the first and last head (heads are independent) ----
 

@@ -154,6 +154,10 @@ def test_forward_full_size_sampled():
          doc_len_min=40, doc_len_max=200),
     dict(B=1, H=3, q_len=400, kv_len=400, q_block=64, kv_block=64,
          score={"kind": "rel_bias", "bias_max": 8.0}, doc_len_min=1, doc_len_max=150),
+    # value head dim other than the query / key head dim
+    dict(B=1, H=2, q_len=600, kv_len=600, d=64, dv=128, doc_len_min=1, doc_len_max=200),
+    dict(B=1, H=2, q_len=450, kv_len=450, d=128, dv=64, q_block=128, kv_block=128,
+         doc_len_min=30, doc_len_max=300),
 ])
 def test_backward_parity(over):
     from test_bwd_gpu import check, oracle_bwd
