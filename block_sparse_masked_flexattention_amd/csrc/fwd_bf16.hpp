@@ -263,6 +263,15 @@ struct Bf16Fwd {
     int lo[NQ], hi[NQ];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) row_interval<MASK>(p, qi[c], lo[c], hi[c]);
+    // the same ends and the row index less 8 g: a block's key offsets then
+    // come from its first key kb0 alone, a wave-uniform value
+    int lo_g[NQ], hi_g[NQ], qi_g[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c) {
+      lo_g[c] = lo[c] - 8 * g;
+      hi_g[c] = hi[c] - 8 * g;
+      qi_g[c] = qi[c] - 8 * g;
+    }
 
     const float c1 = p.c1;
     // Relative bias -slope_h (q - kv) in units of the raw score (c1 s + bias
@@ -363,21 +372,22 @@ struct Bf16Fwd {
     }
 
     // S^T block b (32 keys) of the step in `cur`, for every query sub-tile,
-    // keys from kvl on (register r: key kvl + 16(r >> 3) + (r & 7)).  With
+    // keys from kb0 on (register r of lane half g: key
+    // kb0 + 8 g + 16(r >> 3) + (r & 7)).  With
     // the relative bias the accumulators start at bias / c1, so that the
     // product leaves c1 s + bias in one FMA, as for the plain score.
-    auto s_block = [&](const lds_t* cur, int b, int kvl, f32x16 (&s)[NQ]) {
+    auto s_block = [&](const lds_t* cur, int b, int kb0, f32x16 (&s)[NQ]) {
       u32x4 kf[D / 16];  // all K fragments of the block in flight at once
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) kf[t] = FLEXATTN_LDS(u32x4, cur + kro[t] + 32 * b * ROWB);
 #pragma unroll
       for (int c = 0; c < NQ; ++c) {
         if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
-          // bias_u (q - kv) for keys kvl + r and kvl + 16 + r, r < 8, as two
+          // bias_u (q - kv) for keys kb0 + 8 g + r and 16 more, r < 8, as two
           // chains of -bias_u steps (no per-register constants).  The empty
           // asm statement keeps the compiler from carrying one call's values
           // over to the next call in registers.
-          float a = bias_u * (float)(qi[c] - kvl);
+          float a = bias_u * (float)(qi_g[c] - kb0);
           asm volatile("" : "+v"(a));
           float x = a, y = a - bias_u16;
 #pragma unroll
@@ -414,8 +424,8 @@ struct Bf16Fwd {
     // p = 2^(c1 s + offset)
     auto exp_score = [&](float sc, float nmc) { return __builtin_amdgcn_exp2f(fmaf(sc, c1, nmc)); };
     // set the keys row c does not see (partial tiles) to `fill`
-    auto mask_block = [&](auto& x, int c, int kvl, float fill) {
-      const int lim_hi = hi[c] - kvl, lim_lo = lo[c] - kvl;
+    auto mask_block = [&](auto& x, int c, int kb0, float fill) {
+      const int lim_hi = hi_g[c] - kb0, lim_lo = lo_g[c] - kb0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 16 * (r >> 3) + (r & 7);
@@ -469,10 +479,9 @@ struct Bf16Fwd {
           if (!__any(any)) continue;
           masked = !__all(all);
         }
-        // register r holds key kvl + 16(r >> 3) + (r & 7)
-        const int kvl = kv0 + 32 * b + 8 * g;
+        const int kb0 = kv0 + 32 * b;  // the block's first key
         f32x16 s[NQ];
-        s_block(cur, b, kvl, s);
+        s_block(cur, b, kb0, s);
 
         // the block's V^T fragments go out before the exponentials
         bf16x8 vf[NE][2];
@@ -492,15 +501,26 @@ struct Bf16Fwd {
           for (int c = 0; c < NQ; ++c) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) pv[c][r] = exp_score(s[c][r], nm[c]);
-            if (masked) mask_block(pv[c], c, kvl, 0.f);
+            if (masked) mask_block(pv[c], c, kb0, 0.f);
             rs[c] = sum16(pv[c]);
             bad |= rs[c] > kPMax;
           }
         }
-        float alpha[NQ];
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) alpha[c] = 1.0f;
+        float alpha[NQ];  // set and read only on the slow path
         const bool rescale = XMAX || __any(bad);  // wave-uniform
+        // The mask flag again, recomputed rather than kept: carried through
+        // the fast path it costs a copy through a vector register on every
+        // block.  (The empty asm statement keeps the compiler from reusing
+        // the first computation.)
+        auto masked_again = [&]() {
+          if constexpr (XMAX) return masked;
+          int k0 = kb0;
+          asm volatile("" : "+s"(k0));
+          bool all = true;
+#pragma unroll
+          for (int c = 0; c < NQ; ++c) all = all && lo[c] <= k0 && hi[c] >= k0 + 31;
+          return partial && !__all(all);
+        };
         if (rescale) {
           // Slow path (a row's first visible keys, or scores that rose by
           // more than log2 kPMax; every block with XMAX): raise the running
@@ -511,11 +531,11 @@ struct Bf16Fwd {
           // fragments live through it).
           if constexpr (!XMAX) {
             asm volatile("" ::: "memory");
-            s_block(cur, b, kvl, s);
+            s_block(cur, b, kb0, s);
           }
 #pragma unroll
           for (int c = 0; c < NQ; ++c) {
-            if (masked) mask_block(s[c], c, kvl, -INFINITY);
+            if (masked_again()) mask_block(s[c], c, kb0, -INFINITY);
             // 16-way max as a v_max3 tree: 8 instructions, depth 3
             const float t0 = max3(s[c][0], s[c][1], s[c][2]);
             const float t1 = max3(s[c][3], s[c][4], s[c][5]);
@@ -528,6 +548,7 @@ struct Bf16Fwd {
             const bool seen = m_new != -INFINITY;
             // rows still at -inf keep alpha = 1 (their sum and output are 0)
             alpha[c] = seen ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.0f;
+            l_run[c] *= alpha[c];
             m_run[c] = m_new;
             // masked scores are -inf here, so a finite offset zeroes them
             const float nm_now = seen ? -m_new : 0.f;
@@ -541,7 +562,7 @@ struct Bf16Fwd {
         bf16x8 pk[NQ][2];
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
-          l_run[c] = fmaf(l_run[c], alpha[c], rs[c]);
+          l_run[c] += rs[c];  // (rescaled by alpha in the slow path)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             unsigned w[4];
