@@ -283,7 +283,13 @@ struct Bf16Fwd {
       bias_u16 = 16.0f * bias_u;
     }
 
-    // ---- tile list: partial tiles, then full tiles ----
+    // ---- tile list: partial tiles, then full tiles, each list walked from
+    // its last entry down.  Lists are ascending, so under causal-type masks
+    // the nearest keys (the diagonal, the largest scores under a decaying
+    // bias) come first, which keeps the lagging offset from being raised
+    // again later; and under a sliding window every wave meets its first
+    // visible keys in the same step, so the slow-path blocks of the four
+    // waves overlap instead of following one another. ----
     const int nk = p.n_kb;
     const int np = min(max(p.kv_num[qb], 0), nk);
     const int nf = min(max(p.fkv_num[qb], 0), nk);
@@ -299,8 +305,9 @@ struct Bf16Fwd {
       const int t = min(base + lane, ntiles - 1);
       int v = 0;
       if (t >= 0) {
-        if (p.contig) v = t < np ? prow[0] + t : frow[0] + (t - np);
-        else v = t < np ? prow[t] : frow[t - np];
+        // (each list from its last entry down)
+        if (p.contig) v = t < np ? prow[0] + (np - 1 - t) : frow[0] + (ntiles - 1 - t);
+        else v = t < np ? prow[np - 1 - t] : frow[ntiles - 1 - t];
       }
       return v;
     };

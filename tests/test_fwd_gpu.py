@@ -120,16 +120,17 @@ def test_reruns_are_deterministic():
 
 def _demoted(bm, with_empty):
     """Same visiting order, but every full tile listed as partial (and, with
-    with_empty, every empty tile appended to the partial list too)."""
+    with_empty, every empty tile listed as partial too).  The kernel walks
+    the partial list from its last entry down, then the full list the same
+    way, so the demoted list is empty + full + partial."""
     kvn, kvi, fkn, fki = (a.cpu() for a in bm.arrays())
     nq, nk = kvi.shape
     n_kvi = torch.zeros_like(kvi)
     n_kvn = torch.zeros_like(kvn)
     for qb in range(nq):
-        lst = list(kvi[qb, :kvn[qb]]) + list(fki[qb, :fkn[qb]])
+        lst = [int(x) for x in fki[qb, :fkn[qb]]] + [int(x) for x in kvi[qb, :kvn[qb]]]
         if with_empty:
-            lst += [kb for kb in range(nk) if kb not in set(int(x) for x in lst)]
-        lst = [int(x) for x in lst]
+            lst = [kb for kb in range(nk) if kb not in set(lst)] + lst
         rest = [kb for kb in range(nk) if kb not in set(lst)]
         n_kvi[qb] = torch.tensor(lst + rest, dtype=torch.int32)
         n_kvn[qb] = len(lst)
