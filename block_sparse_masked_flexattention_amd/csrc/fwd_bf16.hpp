@@ -444,8 +444,12 @@ struct Bf16Fwd {
 
     // One step: everything reads buf[B]; step n + NSTAGE - 1 is loaded into
     // the buffer step n - 1 used.
-    auto step = [&](auto buf_tag, int n) {
+    auto step = [&](auto buf_tag, int n, auto exact_tag) {
       constexpr int B = decltype(buf_tag)::value;
+      // EX: every block of this step takes the exact running-max update
+      // (with XMAX always; otherwise on the first step, where no row has
+      // met a key yet and the fast path could only fail)
+      constexpr bool EX = XMAX || decltype(exact_tag)::value != 0;
       lds_t* cur = buf[B];
       const int t = n / SPT, part = n % SPT;
       if (t >= win_base + 64) {  // slide the index window
@@ -503,7 +507,7 @@ struct Bf16Fwd {
         // gives +inf and fails the check).
         float pv[NQ][16], rs[NQ];
         bool bad = false;
-        if constexpr (!XMAX) {
+        if constexpr (!EX) {
 #pragma unroll
           for (int c = 0; c < NQ; ++c) {
 #pragma unroll
@@ -514,13 +518,13 @@ struct Bf16Fwd {
           }
         }
         float alpha[NQ];  // set and read only on the slow path
-        const bool rescale = XMAX || __any(bad);  // wave-uniform
+        const bool rescale = EX || __any(bad);  // wave-uniform
         // The mask flag again, recomputed rather than kept: carried through
         // the fast path it costs a copy through a vector register on every
         // block.  (The empty asm statement keeps the compiler from reusing
         // the first computation.)
         auto masked_again = [&]() {
-          if constexpr (XMAX) return masked;
+          if constexpr (EX) return masked;
           int k0 = kb0;
           asm volatile("" : "+s"(k0));
           bool all = true;
@@ -536,7 +540,7 @@ struct Bf16Fwd {
           // the block's scores (the empty asm statement makes the compiler
           // read K from LDS again instead of keeping the fast path's
           // fragments live through it).
-          if constexpr (!XMAX) {
+          if constexpr (!EX) {
             asm volatile("" ::: "memory");
             s_block(cur, b, kb0, s);
           }
@@ -616,17 +620,31 @@ struct Bf16Fwd {
     }
     step_barrier(NSTAGE - 2);
     // whole rounds of NSTAGE steps, straight-line, then the remainder
+    // (with two buffers the first step is peeled off and takes the exact
+    // update: a row's first visible keys cost one pass instead of a failed
+    // fast pass and a second one)
+    constexpr Int<0> FAST{};
     int n = 0;
-    for (; n + NSTAGE <= nsteps; n += NSTAGE) {
-      step(Int<0>(), n);
-      step(Int<1>(), n + 1);
-      if constexpr (NSTAGE > 2) step(Int<2 % NSTAGE>(), n + 2);
-      if constexpr (NSTAGE > 3) step(Int<3 % NSTAGE>(), n + 3);
+    if constexpr (NSTAGE == 2) {
+      if (nsteps > 0) step(Int<0>(), 0, Int<1>());
+      n = 1;
+      for (; n + 2 <= nsteps; n += 2) {
+        step(Int<1>(), n, FAST);
+        step(Int<0>(), n + 1, FAST);
+      }
+      if (n < nsteps) step(Int<1>(), n, FAST);
+    } else {
+      for (; n + NSTAGE <= nsteps; n += NSTAGE) {
+        step(Int<0>(), n, FAST);
+        step(Int<1>(), n + 1, FAST);
+        if constexpr (NSTAGE > 2) step(Int<2 % NSTAGE>(), n + 2, FAST);
+        if constexpr (NSTAGE > 3) step(Int<3 % NSTAGE>(), n + 3, FAST);
+      }
+      if (n < nsteps) step(Int<0>(), n, FAST);
+      if (n + 1 < nsteps) step(Int<1 % NSTAGE>(), n + 1, FAST);
+      if constexpr (NSTAGE > 2)
+        if (n + 2 < nsteps) step(Int<2 % NSTAGE>(), n + 2, FAST);
     }
-    if (n < nsteps) step(Int<0>(), n);
-    if (n + 1 < nsteps) step(Int<1 % NSTAGE>(), n + 1);
-    if constexpr (NSTAGE > 2)
-      if (n + 2 < nsteps) step(Int<2 % NSTAGE>(), n + 2);
     wait_vmcnt<0>();  // leave no load in flight behind the kernel
 
     // ---- epilogue: out = acc / l, lse = (m + log2 l) ln 2, max = m ln 2 ----
