@@ -274,3 +274,32 @@ def test_many_items_per_workgroup(kv_block):
     cfg = workload("prefix_causal", B=16, H=64, q_len=200, kv_len=200,
                    mask={"kind": "prefix_causal", "prefix": 70}, q_block=128, kv_block=kv_block)
     _full_compare(cfg, "fp32")
+
+
+@pytest.mark.parametrize("name,over", [
+    ("prefix_causal", dict(B=2, H=2, q_len=333, kv_len=333, mask={"kind": "prefix_causal", "prefix": 100})),
+    ("sliding_window", dict(B=1, H=3, q_len=461, kv_len=461)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=297, kv_len=297)),
+    ("prefix_causal", dict(B=1, H=2, q_len=201, kv_len=201, dv=128, mask={"kind": "causal"})),
+])
+def test_bf16_out_rows_stay_inside_the_tensor(name, over):
+    """bf16 output of ragged lengths (the q-block past the last row still
+    runs): every row matches the oracle and nothing past the end of the
+    output tensor is written."""
+    cfg = workload(name, **over)
+    q, k, v = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    B, H, Lq, Dv = cfg["B"], cfg["H"], cfg["q_len"], cfg.get("dv", cfg["d"])
+    n = B * H * Lq * Dv
+    pad = 64 * 1024
+    sentinel = -12345.0  # exact in bf16
+    flat = torch.full((n + pad,), sentinel, dtype=torch.bfloat16, device=dev)
+    out = flat[:n].view(B, H, Lq, Dv)
+    bm = fa.build_block_mask(cfg["mask"], Lq, cfg["kv_len"], cfg["q_block"], cfg["kv_block"], device=dev)
+    fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out)
+    torch.cuda.synchronize()
+    assert bool((flat[n:] == sentinel).all()), "write past the end of the output"
+    ref_out, ref_lse = oracle_rows(cfg, q, k, v)
+    compare(out.double().cpu().numpy().reshape(-1, Dv), None, ref_out, ref_lse, "bf16", "bf16",
+            what=name)
