@@ -139,5 +139,40 @@ __device__ inline void write_out_row(const FwdParams& p, size_t row, int D, int 
     }
 }
 
+// Store the 32 rows of a wave's accumulators as bf16 through LDS.  The
+// accumulators are laid out like O^T: lane (lq, g) holds, in register
+// 4a + i of column block e, column 32e + 8a + 4g + i of row lq.  Each lane
+// writes its 8-byte pieces into the wave's own region `reg` (32 * 64 * NE
+// bytes, 16-byte chunks XOR-swizzled by row), then the wave stores the rows
+// as 16-byte pieces, 64 lanes covering whole rows, to og + row * 64 * NE;
+// rows at or past `nrows` are not written.  Directly from the accumulator
+// layout every store instruction would write 8 bytes into each of 32 rows.
+// The caller guarantees that no other wave touches `reg` meanwhile.
+template <int NE>
+__device__ inline void store_rows_bf16_lds(__attribute__((address_space(3))) char* reg, char* og,
+                                           int nrows, const f32x16 (&a)[NE], float f, int lane) {
+  constexpr int OROW = 64 * NE;  // bytes per row
+  constexpr int OCH = OROW / 16;  // 16-byte chunks per row
+  const int lq = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x4 w = {(__bf16)(a[e][4 * q] * f), (__bf16)(a[e][4 * q + 1] * f),
+                        (__bf16)(a[e][4 * q + 2] * f), (__bf16)(a[e][4 * q + 3] * f)};
+      *(__attribute__((address_space(3))) bf16x4*)(reg + lq * OROW +
+                                                    (((4 * e + q) ^ (lq & 7)) << 4) + 8 * g) = w;
+    }
+  constexpr int RPI = 64 / OCH;  // rows per store instruction
+  const int cc = lane % OCH;
+#pragma unroll
+  for (int j = 0; j < 32 / RPI; ++j) {
+    const int r = j * RPI + lane / OCH;
+    const u32x4 v =
+        *(__attribute__((address_space(3))) u32x4*)(reg + r * OROW + ((cc ^ (r & 7)) << 4));
+    if (r < nrows) *reinterpret_cast<u32x4*>(og + (size_t)r * OROW + cc * 16) = v;
+  }
+}
+
 }  // namespace fwd
 }  // namespace flexattn

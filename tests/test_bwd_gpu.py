@@ -275,3 +275,40 @@ def test_rel_bias_4k():
     got = run_bwd(cfg, q, k, v, dout, dlse)
     ref = oracle_bwd(cfg, q, k, v, dout, dlse)
     check(got, ref, torch.float32, "rel_bias 4k")
+
+
+@pytest.mark.parametrize("name,over", [
+    ("prefix_causal", dict(B=2, H=2, q_len=333, kv_len=301, mask={"kind": "prefix_causal", "prefix": 100})),
+    ("sliding_window", dict(B=1, H=3, q_len=461, kv_len=461)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=297, kv_len=297)),
+    ("prefix_causal", dict(B=1, H=2, q_len=201, kv_len=201, dv=128, mask={"kind": "causal"})),
+    ("long_causal_d128", dict(B=1, H=1, q_len=150, kv_len=230, dv=64, q_block=128, kv_block=64,
+                              mask={"kind": "noop"})),
+])
+def test_bf16_grads_stay_inside_their_tensors(name, over):
+    """bf16 dq, dk, dv of ragged lengths: they match the oracle, and nothing
+    past the end of any gradient tensor is written."""
+    cfg = workload(name, **over)
+    cfg["scale"] = fa.default_scale(cfg["d"])
+    q, k, v = make_inputs(cfg)
+    dout, _ = make_grad_inputs(cfg)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    args = (cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+    bm = fa.build_block_mask(*args, device=DEV)
+    bmt = fa.build_block_mask_t(*args, device=DEV)
+    out, lse = fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out_dtype=torch.bfloat16,
+                      return_lse=True)
+    pad = 64 * 1024
+    sentinel = -12345.0  # exact in bf16
+    grads = []
+    for shape in (qd.shape, kd.shape, vd.shape):
+        n = int(np.prod(shape))
+        flat = torch.full((n + pad,), sentinel, dtype=torch.bfloat16, device=DEV)
+        grads.append((flat, flat[:n].view(shape)))
+    fa.bwd(qd, kd, vd, out, dod, lse, bm, bmt, cfg["score"], cfg["scale"],
+           grad_dtype=torch.bfloat16, dq=grads[0][1], dk=grads[1][1], dv=grads[2][1])
+    torch.cuda.synchronize()
+    for nm, (flat, g) in zip(("dq", "dk", "dv"), grads):
+        assert bool((flat[g.numel():] == sentinel).all()), "write past the end of " + nm
+    got = tuple(g.double().cpu().numpy() for _, g in grads)
+    check(got, oracle_bwd(cfg, q, k, v, dout), torch.bfloat16, "%s %s" % (name, over))
