@@ -655,7 +655,6 @@ struct Bf16Fwd {
     // whole 16-byte pieces, 64 lanes covering contiguous rows, instead of
     // 8-byte pieces scattered over 32 rows.
     constexpr int OROW = DV * 2;       // bytes per output row
-    constexpr int OCH = OROW / 16;     // 16-byte chunks per output row
     constexpr bool LDS_OUT = NQ == 1 && NW * 32 * OROW <= STAGE + STAGEV;
     const bool lds_out = LDS_OUT && p.out_bf16;
 #pragma unroll
@@ -663,29 +662,10 @@ struct Bf16Fwd {
       const float l_tot = l_run[c] + xor32(l_run[c]);
       const bool live = p.safe_rows || l_tot > 0.f;
       const float inv = live ? 1.0f / l_tot : 0.f;
-      if (lds_out) {
-        lds_t* reg = buf[0] + wave * 32 * OROW;
-        // lane (lq, g) holds columns 32e + 8a + 4g .. + 3 of row lq:
-        // 8 bytes at chunk 4e + a, half g; chunks XOR-swizzled by row
-#pragma unroll
-        for (int e = 0; e < NE; ++e)
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const bf16x4 w = {(__bf16)(o[c][e][4 * a] * inv), (__bf16)(o[c][e][4 * a + 1] * inv),
-                              (__bf16)(o[c][e][4 * a + 2] * inv), (__bf16)(o[c][e][4 * a + 3] * inv)};
-            FLEXATTN_LDS(bf16x4, reg + lq * OROW + (((4 * e + a) ^ (lq & 7)) << 4) + 8 * g) = w;
-          }
-        constexpr int RPI = 64 / OCH;  // rows per store instruction
-        const int cc = lane % OCH;
-        char* og = static_cast<char*>(p.out) + (head_q + (size_t)(q0 + wave * 32)) * OROW;
-#pragma unroll
-        for (int j = 0; j < 32 / RPI; ++j) {
-          const int r = j * RPI + lane / OCH;
-          const u32x4 v = FLEXATTN_LDS(u32x4, reg + r * OROW + ((cc ^ (r & 7)) << 4));
-          if (q0 + wave * 32 + r < p.q_len)
-            *reinterpret_cast<u32x4*>(og + (size_t)r * OROW + cc * 16) = v;
-        }
-      }
+      if (lds_out)
+        store_rows_bf16_lds<NE>(buf[0] + wave * 32 * OROW,
+                                static_cast<char*>(p.out) + (head_q + (size_t)(q0 + wave * 32)) * OROW,
+                                p.q_len - (q0 + wave * 32), o[c], inv, lane);
       if (qi[c] < p.q_len) {
         if (!lds_out) write_out_row<NE>(p, head_q + qi[c], DV, g, o[c], inv);
         if (p.lse != nullptr && g == 0)
