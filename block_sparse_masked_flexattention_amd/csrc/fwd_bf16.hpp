@@ -71,42 +71,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_t;
 #define FLEXATTN_LDS(T, ptr) (*(__attribute__((address_space(3))) T*)(ptr))
 
-// Query sub-tiles of 32 rows per wave.  Two sub-tiles halve the LDS reads
-// per FLOP but need about twice the registers; on the 4096-long
-// prefix-or-causal workload one sub-tile per wave (more waves in flight) was
-// measured faster, 565 vs 467 TFLOP/s.
-template <int D, int QB, int KB>
-constexpr int bf16_nq() {
-#ifdef FLEXATTN_NQ
-  return (QB % (32 * FLEXATTN_NQ) == 0) ? FLEXATTN_NQ : 1;
-#else
-  return 1;
-#endif
-}
-
 template <int V>
 struct Int {
   static constexpr int value = V;
 };
-
-// Keys per step (one LDS stage) and number of stage buffers.  A step's K and
-// V arrive NSTAGE - 1 steps ahead of their use.
-template <int D, int QB, int KB>
-constexpr int bf16_ks() {
-#ifdef FLEXATTN_KS
-  return FLEXATTN_KS;
-#else
-  return 64;
-#endif
-}
-template <int D, int QB, int KB>
-constexpr int bf16_nstage() {
-#ifdef FLEXATTN_NSTAGE
-  return FLEXATTN_NSTAGE;
-#else
-  return 2;
-#endif
-}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -122,11 +90,19 @@ __device__ inline void wait_vmcnt() {
 // from the query / key head dim D.
 template <int D, int DV, int QB, int KB, int MASK, int SCORE, bool SUB, bool XMAX>
 struct Bf16Fwd {
-  static constexpr int NQ = bf16_nq<D, QB, KB>();
+  // One 32-row query sub-tile per wave.  (Two sub-tiles per wave halve the
+  // LDS reads per FLOP but need about twice the registers; on the 4096-long
+  // prefix-or-causal workload one sub-tile per wave, with more waves in
+  // flight, measured faster: 565 vs 467 TFLOP/s.)
+  static constexpr int NQ = 1;
   static constexpr int NW = QB / (32 * NQ);  // waves per work-group
   static constexpr int NT = 64 * NW;         // threads per work-group
-  static constexpr int KS = bf16_ks<D, QB, KB>();          // keys per step
-  static constexpr int NSTAGE = bf16_nstage<D, QB, KB>();  // LDS stage buffers
+  // Keys per step (one LDS stage buffer) and stage buffers: a step's K and V
+  // arrive one step ahead of their use.  (Three or four buffers, with 32- or
+  // 64-key steps, measured flat or slower: at head dim 64 a third buffer
+  // costs a work-group per CU.)
+  static constexpr int KS = 64;
+  static constexpr int NSTAGE = 2;
   static constexpr int SPT = KB / KS;        // steps per block-mask tile
   static constexpr int NBS = KS / 32;        // 32-key blocks per step
   static constexpr int NE = DV / 32;         // 32-column blocks of the value head dim
@@ -138,7 +114,6 @@ struct Bf16Fwd {
   static constexpr int CPRV = ROWBV / 16;    // 16-byte chunks per V row
   static constexpr int NDMA = KS * CPR / (64 * NW);    // 16-byte K loads per lane per step
   static constexpr int NDMAV = KS * CPRV / (64 * NW);  // 16-byte V loads per lane per step
-  static constexpr int DMA_PER_STEP = NDMA + NDMAV;    // vector-memory instructions per step
   // Probabilities are taken against a running offset that may lag the row
   // max; a block whose probabilities would exceed kPMax raises it.
   static constexpr float kPMax = 65536.0f;
@@ -146,20 +121,13 @@ struct Bf16Fwd {
   // head dim 64 (<= 128 VGPRs), 2 for 128, and never more than the LDS
   // allows (NSTAGE stage buffers of K and V per work-group, 160 KiB per CU).
   static constexpr int LDS_WAVES = (kLdsBytes / (NSTAGE * (STAGE + STAGEV))) * NW / 4;
-#ifdef FLEXATTN_WAVES
-  static constexpr int REG_WAVES = FLEXATTN_WAVES;
-#else
   static constexpr int REG_WAVES = (D == 64 && DV == 64) ? 4 : 2;
-#endif
   static constexpr int WAVES_PER_SIMD =
       LDS_WAVES < 1 ? 1 : (LDS_WAVES < REG_WAVES ? LDS_WAVES : REG_WAVES);
-  static_assert(KS == 32 || KS == 64, "step size");
-  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "stage count");
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
   static_assert(NDMAV * 64 * NW == KS * CPRV, "step split (V)");
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(DV == 64 || DV == 128, "value head dim");
-  static_assert((NSTAGE - 2) * DMA_PER_STEP < 64, "vmcnt range");
 
   // K: row m, 16-byte chunk c at chunk c ^ kswz(m)
   __device__ static inline int kswz(int m) {
@@ -181,33 +149,23 @@ struct Bf16Fwd {
     return (a[0] + a[1]) + (a[2] + a[3]);
   }
 
-  // End of a step: this wave's loads for the next step are complete (those
-  // of later steps may stay in flight: `later` of them were issued), then
-  // the work-group barrier.  The empty asm statements keep the compiler from
-  // moving memory accesses across the barrier.
-  __device__ static inline void step_barrier(int later) {
-    if constexpr (NSTAGE >= 4) {
-      if (later >= 2) wait_vmcnt<2 * DMA_PER_STEP>();
-      else if (later == 1) wait_vmcnt<DMA_PER_STEP>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NSTAGE == 3) {
-      if (later >= 1) wait_vmcnt<DMA_PER_STEP>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+  // End of a step: this wave's loads of the next step are complete, then
+  // the work-group barrier (every wave's part of the next step is in LDS and
+  // every wave is done reading the buffer the next step's loads overwrite).
+  // The empty asm statements keep the compiler from moving memory accesses
+  // across the barrier.
+  __device__ static inline void step_barrier() {
+    wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
 
   __device__ static void run(const FwdParams& p) {
-    // one distinct LDS variable per stage buffer (unused ones are tiny)
+    // one distinct LDS variable per stage buffer
     __shared__ __attribute__((aligned(16))) char sb0[STAGE + STAGEV];
     __shared__ __attribute__((aligned(16))) char sb1[STAGE + STAGEV];
-    __shared__ __attribute__((aligned(16))) char sb2[NSTAGE > 2 ? STAGE + STAGEV : 16];
-    __shared__ __attribute__((aligned(16))) char sb3[NSTAGE > 3 ? STAGE + STAGEV : 16];
-    lds_t* const buf[4] = {(lds_t*)sb0, (lds_t*)sb1, (lds_t*)sb2, (lds_t*)sb3};
+    lds_t* const buf[2] = {(lds_t*)sb0, (lds_t*)sb1};
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,8 +400,8 @@ struct Bf16Fwd {
       }
     };
 
-    // One step: everything reads buf[B]; step n + NSTAGE - 1 is loaded into
-    // the buffer step n - 1 used.
+    // One step: everything reads buf[B]; step n + 1 is loaded into the
+    // other buffer (which step n - 1 used).
     auto step = [&](auto buf_tag, int n, auto exact_tag) {
       constexpr int B = decltype(buf_tag)::value;
       // EX: every block of this step takes the exact running-max update
@@ -461,15 +419,7 @@ struct Bf16Fwd {
       const int kv0 = kb * KB + part * KS;
       // a listed-full tile at a ragged edge is still handled as partial
       const bool partial = t < np || q_ragged || kb * KB + KB > p.kv_len;
-      // With more than two buffers every step issues the same loads (past
-      // the last step it reloads the last one into a buffer nobody reads),
-      // so the compiler can count them and wait only for the buffer being
-      // read.  With two, each barrier waits for everything anyway.
-      if constexpr (NSTAGE == 2) {
-        if (n + 1 < nsteps) dma(buf[(B + 1) % 2], n + 1);
-      } else {
-        dma(buf[(B + NSTAGE - 1) % NSTAGE], min(n + NSTAGE - 1, nsteps - 1));
-      }
+      if (n + 1 < nsteps) dma(buf[B ^ 1], n + 1);
 
 #pragma unroll
       for (int b = 0; b < NBS; ++b) {
@@ -608,50 +558,32 @@ struct Bf16Fwd {
         }
         __builtin_amdgcn_s_setprio(0);
       }
-      // the loads of steps n + 2 .. n + NSTAGE - 1 may stay in flight
-      step_barrier(NSTAGE - 2);
+      step_barrier();
     };
 
-    // prologue: steps 0 .. NSTAGE - 2 in flight (clamped like the step
-    // loads), then wait for step 0
-    if (nsteps > 0) {
-#pragma unroll
-      for (int m = 0; m < NSTAGE - 1; ++m) dma(buf[m], min(m, nsteps - 1));
-    }
-    step_barrier(NSTAGE - 2);
-    // whole rounds of NSTAGE steps, straight-line, then the remainder
-    // (with two buffers the first step is peeled off and takes the exact
-    // update: a row's first visible keys cost one pass instead of a failed
-    // fast pass and a second one)
+    // prologue: step 0 in flight, then wait for it
+    if (nsteps > 0) dma(buf[0], 0);
+    step_barrier();
+    // pairs of steps, straight-line, then the remainder; the first step is
+    // peeled off and takes the exact update: a row's first visible keys cost
+    // one pass instead of a failed fast pass and a second one
     constexpr Int<0> FAST{};
     int n = 0;
-    if constexpr (NSTAGE == 2) {
-      if (nsteps > 0) step(Int<0>(), 0, Int<1>());
-      n = 1;
-      for (; n + 2 <= nsteps; n += 2) {
-        step(Int<1>(), n, FAST);
-        step(Int<0>(), n + 1, FAST);
-      }
-      if (n < nsteps) step(Int<1>(), n, FAST);
-    } else {
-      for (; n + NSTAGE <= nsteps; n += NSTAGE) {
-        step(Int<0>(), n, FAST);
-        step(Int<1>(), n + 1, FAST);
-        if constexpr (NSTAGE > 2) step(Int<2 % NSTAGE>(), n + 2, FAST);
-        if constexpr (NSTAGE > 3) step(Int<3 % NSTAGE>(), n + 3, FAST);
-      }
-      if (n < nsteps) step(Int<0>(), n, FAST);
-      if (n + 1 < nsteps) step(Int<1 % NSTAGE>(), n + 1, FAST);
-      if constexpr (NSTAGE > 2)
-        if (n + 2 < nsteps) step(Int<2 % NSTAGE>(), n + 2, FAST);
+    if (nsteps > 0) step(Int<0>(), 0, Int<1>());
+    n = 1;
+    for (; n + 2 <= nsteps; n += 2) {
+      step(Int<1>(), n, FAST);
+      step(Int<0>(), n + 1, FAST);
     }
+    if (n < nsteps) step(Int<1>(), n, FAST);
     wait_vmcnt<0>();  // leave no load in flight behind the kernel
 
     // ---- epilogue: out = acc / l, lse = (m + log2 l) ln 2, max = m ln 2 ----
     // (with ROWS_GUARANTEED_SAFE the l = 0 guards are left out)
     // bf16 output goes through LDS: each wave writes its 32 rows into its
     // own region of the first stage buffer (free here: every wave is past
-    // the last step barrier and no load is in flight), then stores them as
+    // the last step barrier and no load is in flight, since each step's
+    // barrier waits for all of its loads), then stores them as
     // whole 16-byte pieces, 64 lanes covering contiguous rows, instead of
     // 8-byte pieces scattered over 32 rows.
     constexpr int OROW = DV * 2;       // bytes per output row

@@ -57,31 +57,40 @@ __device__ inline int swap23(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// Work-group -> (head bh, q-block qb).  Work-groups are dispatched round-robin
-// over the 8 XCDs (work-group w to XCD w % 8), and each XCD has its own L2.
+// Work items (head bh, q-block qb) split over the 8 XCDs, each of which has
+// its own L2.  n_items = heads * n_qb; item k of XCD xcd (k = 0, 1, ...)
+// maps to (bh, qb); returns false once k is past that XCD's items.
 //  * When the number of heads is a multiple of 8, XCD x owns heads
-//    [x H/8, (x+1) H/8) and runs their q-blocks last-to-first across all of
-//    them: every head's last q-block, then every head's second-to-last, ...
-//    Under a causal-like mask the last q-blocks are the longest, so long work
-//    starts first and the short blocks fill the tail, while each head's K/V
-//    stay in one XCD's L2.
-//  * Otherwise each XCD gets a contiguous range of (head, q-block) work,
+//    [x H/8, (x+1) H/8) and orders their q-blocks last-to-first across all
+//    of them: every head's last q-block, then every head's second-to-last,
+//    ...  Under a causal-like mask the last q-blocks are the longest, so
+//    long work starts first and the short blocks fill the tail, while each
+//    head's K/V stay in one XCD's L2.
+//  * Otherwise each XCD gets a contiguous range of (head, q-block) items,
 //    q-blocks last-to-first within a head.
-__device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
-  const int nwg = gridDim.x, w = blockIdx.x;
-  const int n_heads = nwg / n_qb;
-  const int xcd = w & 7, k = w >> 3;
+__device__ inline bool xcd_item(int n_items, int n_qb, int xcd, int k, int& bh, int& qb) {
+  const int n_heads = n_items / n_qb;
   if ((n_heads & 7) == 0) {
     const int hx = n_heads >> 3;
+    if (k >= hx * n_qb) return false;
     const int rank = k / hx;
     bh = xcd * hx + (k - rank * hx);
     qb = n_qb - 1 - rank;
-    return;
+    return true;
   }
-  const int per = nwg >> 3, rem = nwg & 7;
+  const int per = n_items >> 3, rem = n_items & 7;
+  if (k >= per + (xcd < rem ? 1 : 0)) return false;
   const int r = xcd * per + min(xcd, rem) + k;
   bh = r / n_qb;
   qb = n_qb - 1 - (r - bh * n_qb);
+  return true;
+}
+
+// One work-group per item: the dispatcher sends work-group w to XCD w % 8,
+// so work-group w takes item w >> 3 of that XCD.
+__device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
+  const int w = blockIdx.x;
+  xcd_item(gridDim.x, n_qb, w & 7, w >> 3, bh, qb);
 }
 
 // Keys visible from query row qi, as one interval [lo, hi] (empty when

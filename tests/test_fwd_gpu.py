@@ -276,6 +276,27 @@ def test_many_items_per_workgroup(kv_block):
     _full_compare(cfg, "fp32")
 
 
+def test_items_without_tiles_between_full_ones():
+    """5120 (head, q-block) work items, several times what the device holds
+    at once: every fifth q-block (the first of each head) has no tile at all
+    (window_min 200 > its last row), so empty items sit between full ones
+    in the dispatch order.  Every row is compared; the empty rows are
+    exactly 0 and -inf."""
+    cfg = workload("sliding_window", B=16, H=64, q_len=520, kv_len=520,
+                   mask={"kind": "sliding_window", "window": 300, "window_min": 200})
+    _full_compare(cfg, "fp32")
+    q, k, v = make_inputs(cfg)
+    out, lse, _ = run_gpu(cfg, q, k, v, out_dtype=torch.bfloat16, lse=True)
+    assert np.all(np.isneginf(lse[:, :, :200])) and np.all(out[:, :, :200] == 0)
+
+
+def test_many_items_head_dim_128():
+    """Head dim 128 (two waves per SIMD, so fewer resident work-groups) with
+    many more short items than resident work-groups, and ragged lengths."""
+    cfg = workload("long_causal_d128", B=8, H=32, q_len=333, kv_len=333)
+    _full_compare(cfg, "bf16")
+
+
 @pytest.mark.parametrize("name,over", [
     ("prefix_causal", dict(B=2, H=2, q_len=333, kv_len=333, mask={"kind": "prefix_causal", "prefix": 100})),
     ("sliding_window", dict(B=1, H=3, q_len=461, kv_len=461)),
