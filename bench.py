@@ -22,6 +22,17 @@ its `cpu_baseline` times the oracle's backward on whole heads.
 `--copy-calibration` instead runs only a plain device-to-device copy of a
 known size, so that rocprofv3's FETCH_SIZE / WRITE_SIZE counters can be
 scaled against it.
+
+`--mfma-peak` runs only the matrix-unit microbenchmark (independent chains
+of v_mfma_f32_32x32x16_bf16, 4 waves per SIMD, HIP-event timed) and prints
+its measured dense bf16 rate and the shader clock it ran at; the default
+forward line carries the same figures in `mfma_peak_measured`.
+
+The default forward line also carries `sliding_window`: the sliding-window
+workload (B=2, H=16, L=8192, window 256, 128x128 tiles) timed the same way
+with the alpha-rescale subtiling off and on, each with its warm and
+cold-cache forward time, its fraction of the bf16 peak and of the HBM
+roofline of its algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -39,6 +50,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector (the fp32-input instance)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_prefix_causal_traffic.txt")
 
 
@@ -78,6 +90,18 @@ def stored_traffic(workload_name: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, q, k, v, target_seconds: float, seed: int = 0):
     """Time the fp64 oracle on randomly sampled query rows of the workload,
     growing the sample until it takes about `target_seconds`."""
@@ -109,6 +133,7 @@ def cpu_baseline(cfg, q, k, v, target_seconds: float, seed: int = 0):
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": "%d query rows drawn uniformly from all B*H*Lq rows of the workload, "
                   "fp64 oracle, %.1f s" % (rows_done, spent),
@@ -140,6 +165,7 @@ def cpu_baseline_bwd(cfg, q, k, v, dout, target_seconds: float):
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": "%d whole heads (of %d) of the workload, fp64 oracle backward, %.1f s"
                   % (heads_done, B * H, spent),
@@ -303,6 +329,111 @@ def write_traffic_file(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     print("\n".join(lines))
 
 
+def mfma_peak(reps: int = 5, iters: int = 20000) -> dict:
+    """Measured dense bf16 matrix rate: the library's probe kernel (4
+    independent v_mfma_f32_32x32x16_bf16 chains per wave, 4 work-groups of 4
+    waves per compute unit) timed with HIP events on its stream, and the
+    shader clock from each wave's cycle and real-time counters."""
+    import torch
+    from block_sparse_masked_flexattention_amd import flexattn as fa
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nwg = 4 * cus
+    stream = torch.cuda.current_stream(dev)
+    fa.mfma_peak_probe(nwg, iters, dev)  # warm-up
+    torch.cuda.synchronize()
+    times, clocks = [], None
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        flops, _, clocks = fa.mfma_peak_probe(nwg, iters, dev)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    c = clocks.cpu().numpy().reshape(-1, 2).astype(np.float64)
+    ghz = float(np.median(0.1 * c[:, 0] / np.maximum(c[:, 1], 1.0)))
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3), "ms": round(ms, 4),
+            "frac_of_published": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "published_at_measured_clock": round(PEAK_BF16_TFLOPS * ghz / 2.4, 1),
+            "kernel": "4 waves/SIMD x 4 independent v_mfma_f32_32x32x16_bf16 chains, %d work-groups"
+                      " x %d rounds" % (nwg, iters)}
+
+
+def fwd_timing(cfg, dmask, qd, kd, vd, steps: int, warmup: int, cold_reps: int,
+               use_subtiling: bool = False) -> dict:
+    """Warm and cold-cache forward times of one workload (HIP events on the
+    launch stream), its fraction of the bf16 peak and, from its algorithmic
+    bytes (q, k, v read once, out written once), of the HBM roofline."""
+    import torch
+    from block_sparse_masked_flexattention_amd import flexattn as fa
+    dev = qd.device
+    B, H, Lq, Lk, D = cfg["B"], cfg["H"], cfg["q_len"], cfg["kv_len"], cfg["d"]
+    Dv = cfg.get("dv", D)
+    out = torch.empty((B, H, Lq, Dv), dtype=qd.dtype, device=dev)
+    bm = fa.build_block_mask(dmask, Lq, Lk, cfg["q_block"], cfg["kv_block"], device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(qd, kd, vd, bm, cfg["score"], cfg["scale"], out=out, use_subtiling=use_subtiling)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    warm = [a.elapsed_time(b) for a, b in evs]
+    cold = []
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(cold_reps):
+        flush.fill_(1.0)
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        run(e)
+        torch.cuda.synchronize()
+        cold.append(e[0].elapsed_time(e[1]))
+    del flush
+    pairs = visible_pairs(cfg["mask"], Lq, Lk)
+    flops = 2.0 * B * H * (D + Dv) * pairs
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    hbm_bytes = float(esz) * B * H * (Lq * D + Lk * D + Lk * Dv + Lq * Dv)
+    ms = float(np.mean(warm))
+    ms_cold = float(np.median(cold)) if cold else None
+    res = {"fwd_ms": round(ms, 5), "fwd_ms_min": round(float(np.min(warm)), 5),
+           "fwd_ms_cold": round(ms_cold, 5) if ms_cold else None,
+           "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "hbm_bytes": hbm_bytes,
+           "hbm_frac": round(hbm_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "hbm_frac_cold": round(hbm_bytes / (ms_cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+           if ms_cold else None}
+    return res
+
+
+def sliding_window_lines(steps: int, warmup: int, cold_reps: int) -> dict:
+    """The sliding-window workload with subtiling off and on (see the module
+    docstring)."""
+    import torch
+    from block_sparse_masked_flexattention_amd.inputs import make_inputs, workload
+    cfg = workload("sliding_window")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in make_inputs(cfg))
+    res = {"config": {"B": cfg["B"], "H": cfg["H"], "q_len": cfg["q_len"], "head_dim": cfg["d"],
+                      "mask": cfg["mask"], "q_block": cfg["q_block"], "kv_block": cfg["kv_block"]}}
+    for sub in (False, True):
+        res["subtiling_on" if sub else "subtiling_off"] = fwd_timing(
+            cfg, cfg["mask"], qd, kd, vd, steps, warmup, cold_reps, use_subtiling=sub)
+    return res
+
+
 def copy_calibration(nbytes: int, reps: int):
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
@@ -333,6 +464,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="only the matrix-unit microbenchmark: measured bf16 peak and clock")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="forward: leave out the sliding-window and matrix-peak figures")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="measure the forward (default) or the backward")
     ap.add_argument("--cold-reps", type=int, default=10,
@@ -356,6 +491,11 @@ def main(argv=None):
 
     if args.copy_calibration:
         copy_calibration(1 << 30, 5)
+        return 0
+    if args.mfma_peak:
+        torch.cuda.set_device(0)
+        fa.load()
+        print(json.dumps({"mfma_peak_measured": mfma_peak()}), flush=True)
         return 0
 
     name = args.workload or BENCH_WORKLOAD
@@ -467,6 +607,12 @@ def main(argv=None):
             "frac": round(achieved / peak, 4), "traffic": traffic,
         },
     }
+    if not args.no_extra and args.workload is None:
+        res["sliding_window"] = sliding_window_lines(max(args.steps, 20), args.warmup,
+                                                     args.cold_reps)
+        peak = mfma_peak()
+        peak["forward_frac_of_measured"] = round(achieved / peak["tflops"], 4)
+        res["mfma_peak_measured"] = peak
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, q, k, v, args.cpu_seconds)
     else:

@@ -307,7 +307,8 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
       rows * v_head_dim > ((int64_t)1 << 40) || krows * v_head_dim > ((int64_t)1 << 40))
     return FLEX_E_INVALID_ARG;
   if (rows == 0 && krows == 0) return FLEX_OK;  // nothing to write
-  if (rows > 0 && (!q || !out || !dout || !lse || !dq || !workspace)) return FLEX_E_INVALID_ARG;
+  // dq may be NULL: WRITE_DQ off (dq is not computed)
+  if (rows > 0 && (!q || !out || !dout || !lse || !workspace)) return FLEX_E_INVALID_ARG;
   if (krows > 0 && (!k || !v || !dk || !dv)) return FLEX_E_INVALID_ARG;
   if (bm->n_q_blocks > 0 && (!bm->kv_num_blocks || !bm->full_kv_num_blocks))
     return FLEX_E_INVALID_ARG;

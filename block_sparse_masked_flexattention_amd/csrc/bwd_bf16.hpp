@@ -750,7 +750,8 @@ hipError_t launch_bwd_one(const BwdParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const long long nq = (long long)p.B * p.H * p.n_qb;
+  // dq == nullptr: WRITE_DQ off, the dq kernel is skipped
+  const long long nq = p.dq != nullptr ? (long long)p.B * p.H * p.n_qb : 0;
   if (nq > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
                        dim3(Bf16BwdDq<D, DV, QB, KB, MASK, SCORE>::NT), 0, s, p);

@@ -23,7 +23,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -35,6 +35,7 @@ EXPORTED = (
     "flex_attn_fwd",
     "flex_attn_bwd_workspace_floats",
     "flex_attn_bwd",
+    "flex_attn_mfma_peak_probe",
 )
 
 
@@ -124,6 +125,8 @@ def load(path: str | None = None):
                                       ctypes.POINTER(ScoreDesc), ctypes.c_float, vp, vp, vp,
                                       i32, vp, vp]
         lib.flex_attn_bwd.restype = i32
+        lib.flex_attn_mfma_peak_probe.argtypes = [i32, i32, vp, vp, vp]
+        lib.flex_attn_mfma_peak_probe.restype = i32
         if lib.flex_attn_abi_version() != ABI_VERSION:
             raise RuntimeError("libflexattn.so ABI version mismatch")
         if path is None:
@@ -183,6 +186,51 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on_device(t, dev: torch.device, name: str, dtype=None, shape=None):
+    """Raise ValueError unless t is a contiguous GPU tensor on `dev` (of
+    `dtype` and `shape` when given): every pointer this binding passes to
+    the library must be device memory the kernels can reach."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda" or t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _check_block_mask(bm, dev: torch.device, q_len: int, kv_len: int):
+    """The block mask's arrays: int32, contiguous, on `dev`, sized for its
+    block counts, and built for these sequence lengths."""
+    if bm.q_len != q_len or bm.kv_len != kv_len:
+        raise ValueError("block mask built for lengths (%d, %d), call has (%d, %d)"
+                         % (bm.q_len, bm.kv_len, q_len, kv_len))
+    nq, nk = block_mask_dims(q_len, kv_len, bm.q_block, bm.kv_block)
+    for a, nm, shp in zip(bm.arrays(), ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                                        "full_kv_indices"), [(nq,), (nq, nk), (nq,), (nq, nk)]):
+        _on_device(a, dev, nm, torch.int32, shp)
+    if is_document(bm.mask):
+        if bm.row_bounds is None:
+            raise ValueError("a document mask needs row_bounds")
+        _on_device(bm.row_bounds, dev, "row_bounds", torch.int32, (2 * q_len,))
+
+
+def _check_block_mask_t(bmt, dev: torch.device, q_len: int, kv_len: int):
+    if bmt.q_len != q_len or bmt.kv_len != kv_len:
+        raise ValueError("transposed block mask built for other lengths")
+    nq, nk = block_mask_dims(q_len, kv_len, bmt.q_block, bmt.kv_block)
+    for a, nm, shp in zip(bmt.arrays(), ("q_num_blocks", "q_indices", "full_q_num_blocks",
+                                         "full_q_indices"), [(nk,), (nk, nq), (nk,), (nk, nq)]):
+        _on_device(a, dev, nm, torch.int32, shp)
+    if is_document(bmt.mask):
+        if bmt.col_bounds is None:
+            raise ValueError("a document mask needs col_bounds")
+        _on_device(bmt.col_bounds, dev, "col_bounds", torch.int32, (2 * kv_len,))
+
+
 @dataclass
 class BlockMask:
     """The kv half of a FlexAttention block mask, on the device."""
@@ -217,18 +265,31 @@ def build_block_mask(mask: dict, q_len: int, kv_len: int, q_block: int, kv_block
     nq, nk = block_mask_dims(q_len, kv_len, q_block, kv_block)
     if out is None:
         dev = torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError("the block mask is built on the GPU: device must be a cuda device")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
         z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
         out = BlockMask(dict(mask), q_len, kv_len, q_block, kv_block,
                         z(nq), z(nq, nk), z(nq), z(nq, nk),
                         z(2 * q_len) if is_document(mask) else None)
+    elif (out.q_len, out.kv_len, out.q_block, out.kv_block) != (q_len, kv_len, q_block, kv_block):
+        raise ValueError("out was made for other lengths or block sizes")
     arrs = out.arrays()
-    for a, shape in zip(arrs, [(nq,), (nq, nk), (nq,), (nq, nk)]):
-        if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
-            raise ValueError("block-mask arrays have the wrong dtype/shape")
-    if is_document(mask) and (out.row_bounds is None or out.row_bounds.numel() < 2 * q_len):
-        raise ValueError("a document mask needs row_bounds of 2 * q_len")
-    md = mask_desc(mask, q_len, kv_len)
     dev = arrs[0].device
+    if dev.type != "cuda":
+        raise ValueError("block-mask arrays must be on a cuda device")
+    for a, nm, shape in zip(arrs, ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                                   "full_kv_indices"), [(nq,), (nq, nk), (nq,), (nq, nk)]):
+        _on_device(a, dev, nm, torch.int32, shape)
+    if is_document(mask):
+        if out.row_bounds is None:
+            raise ValueError("a document mask needs row_bounds of 2 * q_len")
+        _on_device(out.row_bounds, dev, "row_bounds", torch.int32, (2 * q_len,))
+    for key in ("q_doc", "kv_doc"):
+        if mask.get(key) is not None:
+            _on_device(mask[key], dev, key, torch.int32)
+    md = mask_desc(mask, q_len, kv_len)
     rb = out.row_bounds.data_ptr() if out.row_bounds is not None else None
     _check(load().flex_attn_build_block_mask(
         ctypes.byref(md), q_len, kv_len, q_block, kv_block,
@@ -261,21 +322,24 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
     for t in (q, k, v):
         if not t.is_contiguous() or t.device.type != "cuda":
             raise ValueError("q/k/v must be contiguous GPU tensors")
+    dev = q.device
+    for t, nm in ((k, "k"), (v, "v")):
+        _on_device(t, dev, nm)
+    _check_block_mask(block_mask, dev, Lq, Lk)
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, H, Lq, Dv), dtype=out_dtype, device=q.device)
     elif out.shape != (B, H, Lq, Dv) or out.dtype not in _DT or not out.is_contiguous():
         raise ValueError("bad out tensor")
+    _on_device(out, dev, "out")
     if return_lse and lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32
-                            or not lse.is_contiguous()):
-        raise ValueError("bad lse tensor")
+    if lse is not None:
+        _on_device(lse, dev, "lse", torch.float32, (B, H, Lq))
     if return_max and max_out is None:
         max_out = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    if max_out is not None and (max_out.shape != (B, H, Lq) or max_out.dtype != torch.float32
-                                or not max_out.is_contiguous()):
-        raise ValueError("bad max_out tensor")
+    if max_out is not None:
+        _on_device(max_out, dev, "max_out", torch.float32, (B, H, Lq))
     sc = score or {"kind": "identity"}
     sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
                    float(sc.get("bias_max", 8.0)))
@@ -328,23 +392,53 @@ def build_block_mask_t(mask: dict, q_len: int, kv_len: int, q_block: int, kv_blo
     nq, nk = block_mask_dims(q_len, kv_len, q_block, kv_block)
     if out is None:
         dev = torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError("the block mask is built on the GPU: device must be a cuda device")
+        if dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
         z = lambda *s: torch.empty(s, dtype=torch.int32, device=dev)
         out = BlockMaskT(dict(mask), q_len, kv_len, q_block, kv_block,
                          z(nk), z(nk, nq), z(nk), z(nk, nq),
                          z(2 * kv_len) if is_document(mask) else None)
+    elif (out.q_len, out.kv_len, out.q_block, out.kv_block) != (q_len, kv_len, q_block, kv_block):
+        raise ValueError("out was made for other lengths or block sizes")
     arrs = out.arrays()
-    for a, shape in zip(arrs, [(nk,), (nk, nq), (nk,), (nk, nq)]):
-        if a.dtype != torch.int32 or tuple(a.shape) != shape or not a.is_contiguous():
-            raise ValueError("transposed block-mask arrays have the wrong dtype/shape")
-    if is_document(mask) and (out.col_bounds is None or out.col_bounds.numel() < 2 * kv_len):
-        raise ValueError("a document mask needs col_bounds of 2 * kv_len")
-    md = mask_desc(mask, q_len, kv_len)
     dev = arrs[0].device
+    if dev.type != "cuda":
+        raise ValueError("transposed block-mask arrays must be on a cuda device")
+    for a, nm, shape in zip(arrs, ("q_num_blocks", "q_indices", "full_q_num_blocks",
+                                   "full_q_indices"), [(nk,), (nk, nq), (nk,), (nk, nq)]):
+        _on_device(a, dev, nm, torch.int32, shape)
+    if is_document(mask):
+        if out.col_bounds is None:
+            raise ValueError("a document mask needs col_bounds of 2 * kv_len")
+        _on_device(out.col_bounds, dev, "col_bounds", torch.int32, (2 * kv_len,))
+    for key in ("q_doc", "kv_doc"):
+        if mask.get(key) is not None:
+            _on_device(mask[key], dev, key, torch.int32)
+    md = mask_desc(mask, q_len, kv_len)
     cb = out.col_bounds.data_ptr() if out.col_bounds is not None else None
     _check(load().flex_attn_build_block_mask_t(
         ctypes.byref(md), q_len, kv_len, q_block, kv_block,
         *[a.data_ptr() for a in arrs], cb, _stream_handle(dev)), "flex_attn_build_block_mask_t")
     return out
+
+
+def mfma_peak_probe(n_workgroups: int, iters: int, device="cuda"):
+    """Launch the matrix-unit peak microbenchmark once on the current stream
+    (see flex_attn_mfma_peak_probe in include/flexattn.h).  Returns (FLOPs
+    of the launch, sink tensor, clocks tensor); the caller times the launch
+    and reads the clocks after synchronising."""
+    dev = torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError("the probe runs on a cuda device")
+    sink = torch.empty(n_workgroups * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(n_workgroups * 4 * 2, dtype=torch.int64, device=dev)
+    _check(load().flex_attn_mfma_peak_probe(n_workgroups, iters, sink.data_ptr(),
+                                            clocks.data_ptr(), _stream_handle(sink.device)),
+           "flex_attn_mfma_peak_probe")
+    flops = float(n_workgroups) * 4 * iters * 4 * 32768
+    return flops, sink, clocks
 
 
 def bwd_workspace_floats(B: int, H: int, q_len: int) -> int:
@@ -359,10 +453,13 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         block_mask_t: BlockMaskT, score: dict | None = None, scale: float | None = None, *,
         dlse: torch.Tensor | None = None, grad_dtype: torch.dtype | None = None,
         workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
-        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None):
+        dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
+        write_dq: bool = True):
     """Gradients (dq, dk, dv) of the masked attention forward.  q/k/v/out/dout
     as in ``fwd`` (out and lse the forward's results), lse float32 [B,H,Lq].
-    v, out, dout and dv may have a value head dim Dv other than q's D."""
+    v, out, dout and dv may have a value head dim Dv other than q's D.
+    ``write_dq=False`` (the WRITE_DQ kernel option) skips dq: the first
+    result is then None."""
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
     Dv = v.shape[3] if v.dim() == 4 else -1
@@ -375,26 +472,37 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     for t in (q, k, v, out, dout):
         if not t.is_contiguous() or t.device.type != "cuda":
             raise ValueError("q/k/v/out/dout must be contiguous GPU tensors")
-    if lse.shape != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("bad lse tensor")
-    if dlse is not None and (dlse.shape != (B, H, Lq) or dlse.dtype != torch.float32
-                             or not dlse.is_contiguous()):
-        raise ValueError("bad dlse tensor")
+    dev = q.device
+    for t, nm in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _on_device(t, dev, nm)
+    _on_device(lse, dev, "lse", torch.float32, (B, H, Lq))
+    if dlse is not None:
+        _on_device(dlse, dev, "dlse", torch.float32, (B, H, Lq))
+    _check_block_mask(block_mask, dev, Lq, Lk)
+    _check_block_mask_t(block_mask_t, dev, Lq, Lk)
     gd = grad_dtype or torch.float32
     if gd not in _DT:
         raise ValueError("grad_dtype must be bfloat16 or float32")
     mk = lambda L, d: torch.empty((B, H, L, d), dtype=gd, device=q.device)
-    dq = mk(Lq, D) if dq is None else dq
+    if write_dq:
+        dq = mk(Lq, D) if dq is None else dq
+    elif dq is not None:
+        raise ValueError("dq given with write_dq=False")
     dk = mk(Lk, D) if dk is None else dk
     dv = mk(Lk, Dv) if dv is None else dv
     for t, L, d in ((dq, Lq, D), (dk, Lk, D), (dv, Lk, Dv)):
+        if t is None:
+            continue
         if t.shape != (B, H, L, d) or t.dtype != gd or not t.is_contiguous():
             raise ValueError("bad gradient tensor")
+        _on_device(t, dev, "gradient")
     nws = bwd_workspace_floats(B, H, Lq)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < nws:
         raise ValueError("workspace too small")
+    else:
+        _on_device(workspace, dev, "workspace", torch.float32)
     sc = score or {"kind": "identity"}
     sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
                    float(sc.get("bias_max", 8.0)))
@@ -405,6 +513,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
         lse.data_ptr(), dlse.data_ptr() if dlse is not None else None, _DT[q.dtype],
         B, H, Lq, Lk, D, Dv, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _DT[gd], workspace.data_ptr(),
+        dq.data_ptr() if dq is not None else None, dk.data_ptr(), dv.data_ptr(), _DT[gd],
+        workspace.data_ptr(),
         _stream_handle(q.device)), "flex_attn_bwd")
     return dq, dk, dv

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 5
+#define FLEXATTN_ABI_VERSION 6
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -285,6 +285,10 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
  *   dq [B, H, q_len, head_dim], dk [B, H, kv_len, head_dim],
  *   dv [B, H, kv_len, v_head_dim] of grad_dtype (BF16 or FP32), 16-byte
  *   aligned, written in full (zero where nothing contributes).
+ *   dq may be NULL: the WRITE_DQ kernel option of the test hunks set to
+ *   False (the flex_attention_backward call there passes it among its
+ *   kernel options).  The dq kernel is then not run, nothing is written in
+ *   its place, and dk and dv are the same as with dq requested.
  *   workspace: device fp32, flex_attn_bwd_workspace_floats() floats, owned by
  *   the caller; its contents on entry are ignored and left undefined.
  * Built instances: in_dtype BF16, head_dim and v_head_dim each 64 or 128,
@@ -299,6 +303,24 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const flex_block_mask* bm, const flex_block_mask_t* bmt,
                       const flex_score_desc* score, float scale, void* dq, void* dk,
                       void* dv, int32_t grad_dtype, float* workspace, void* stream);
+
+/* Measurement helper, not part of the attention path: the matrix-unit peak
+ * the forward's rate is compared with.  Launches n_workgroups work-groups of
+ * 256 threads (4 waves); every wave runs `iters` rounds of 4 independent
+ * v_mfma_f32_32x32x16_bf16 (32 * 32 * 16 * 2 = 32768 FLOPs each), so the
+ * launch does n_workgroups * 4 * iters * 4 * 32768 FLOPs; the caller times
+ * it on `stream`.  Launch 4 work-groups per compute unit (4 waves per SIMD)
+ * or more to fill the part.
+ *   sink: device fp32 [n_workgroups * 256] (receives sums of the
+ *   accumulators, so that no product is dead code).
+ *   clocks: device uint64 [n_workgroups * 4 * 2]; wave w writes
+ *   clocks[2w] = shader clock cycles (s_memtime) and clocks[2w + 1] = ticks
+ *   of the 100 MHz real-time counter (s_memrealtime) over its chains, so the
+ *   shader clock under this load is 0.1 GHz * clocks[2w] / clocks[2w + 1].
+ * Errors: FLEX_E_INVALID_ARG (non-positive sizes, null or misaligned
+ * pointers), FLEX_E_HIP. */
+int32_t flex_attn_mfma_peak_probe(int32_t n_workgroups, int32_t iters, float* sink,
+                                  uint64_t* clocks, void* stream);
 
 #ifdef __cplusplus
 }

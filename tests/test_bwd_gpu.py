@@ -312,3 +312,35 @@ def test_bf16_grads_stay_inside_their_tensors(name, over):
         assert bool((flat[g.numel():] == sentinel).all()), "write past the end of " + nm
     got = tuple(g.double().cpu().numpy() for _, g in grads)
     check(got, oracle_bwd(cfg, q, k, v, dout), torch.bfloat16, "%s %s" % (name, over))
+
+
+@pytest.mark.parametrize("name,over", [
+    ("prefix_causal", dict(B=1, H=2, q_len=333, kv_len=333, mask={"kind": "prefix_causal", "prefix": 100})),
+    ("long_causal_d128", dict(B=1, H=2, q_len=300, kv_len=300)),
+    ("sliding_window", dict(B=1, H=2, q_len=461, kv_len=461, dv=128)),
+])
+def test_write_dq_off(name, over):
+    """WRITE_DQ off (dq = NULL): the launcher skips the dq kernel, and dk
+    and dv are bitwise the same as with dq requested (and within the
+    backward bar of the oracle)."""
+    cfg = workload(name, **over)
+    q, k, v = make_inputs(cfg)
+    dout, _ = make_grad_inputs(cfg)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, dout))
+    args = (cfg["mask"], cfg["q_len"], cfg["kv_len"], cfg["q_block"], cfg["kv_block"])
+    bm = fa.build_block_mask(*args, device=DEV)
+    bmt = fa.build_block_mask_t(*args, device=DEV)
+    out, lse = fa.fwd(qd, kd, vd, bm, cfg.get("score"), cfg["scale"], return_lse=True)
+    dq, dk, dv = fa.bwd(qd, kd, vd, out, dod, lse, bm, bmt, cfg.get("score"), cfg["scale"],
+                        grad_dtype=torch.bfloat16)
+    none, dk2, dv2 = fa.bwd(qd, kd, vd, out, dod, lse, bm, bmt, cfg.get("score"), cfg["scale"],
+                            grad_dtype=torch.bfloat16, write_dq=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    # and the gradients themselves are the oracle's (dk, dv)
+    refs = oracle_bwd(cfg, q, k, v, dout)
+    for name_g, g, r in (("dk", dk2, refs[1]), ("dv", dv2, refs[2])):
+        gn = g.double().cpu().numpy()
+        bound = TOL_BWD * np.abs(r).max() + ATOL_BWD + bf16_half_ulp(r)
+        assert np.all(np.abs(gn - r) <= bound), name_g
