@@ -53,6 +53,8 @@ const char* flex_attn_strerror(int32_t code) {
       return "unsupported configuration (no kernel instance for it)";
     case FLEX_E_HIP:
       return "HIP launch error";
+    case FLEX_E_SCRATCH_LIMIT:
+      return "too large for flex_attn_bwd_noalloc's scratch (2 * B * H * q_len floats)";
     default:
       return "unknown status code";
   }

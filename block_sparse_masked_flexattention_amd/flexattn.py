@@ -18,12 +18,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflexattn.so")
 
-FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP = 0, 1, 2, 3
+FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP, FLEX_E_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_FLOATS = 1 << 23
 DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -35,6 +36,7 @@ EXPORTED = (
     "flex_attn_fwd",
     "flex_attn_bwd_workspace_floats",
     "flex_attn_bwd",
+    "flex_attn_bwd_noalloc",
     "flex_attn_mfma_peak_probe",
 )
 
@@ -125,6 +127,12 @@ def load(path: str | None = None):
                                       ctypes.POINTER(ScoreDesc), ctypes.c_float, vp, vp, vp,
                                       i32, vp, vp]
         lib.flex_attn_bwd.restype = i32
+        lib.flex_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                              i32, i32, i32, ctypes.POINTER(BlockMaskStruct),
+                                              ctypes.POINTER(BlockMaskTStruct),
+                                              ctypes.POINTER(ScoreDesc), ctypes.c_float, vp, vp,
+                                              vp, i32, vp]
+        lib.flex_attn_bwd_noalloc.restype = i32
         lib.flex_attn_mfma_peak_probe.argtypes = [i32, i32, vp, vp, vp]
         lib.flex_attn_mfma_peak_probe.restype = i32
         if lib.flex_attn_abi_version() != ABI_VERSION:
@@ -454,12 +462,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         dlse: torch.Tensor | None = None, grad_dtype: torch.dtype | None = None,
         workspace: torch.Tensor | None = None, dq: torch.Tensor | None = None,
         dk: torch.Tensor | None = None, dv: torch.Tensor | None = None,
-        write_dq: bool = True):
+        write_dq: bool = True, noalloc: bool = False):
     """Gradients (dq, dk, dv) of the masked attention forward.  q/k/v/out/dout
     as in ``fwd`` (out and lse the forward's results), lse float32 [B,H,Lq].
     v, out, dout and dv may have a value head dim Dv other than q's D.
     ``write_dq=False`` (the WRITE_DQ kernel option) skips dq: the first
-    result is then None."""
+    result is then None.  ``noalloc=True`` calls flex_attn_bwd_noalloc,
+    whose workspace is the library's own per-GPU scratch (no workspace
+    argument; calls that overlap on one GPU race on it)."""
     B, H, Lq, D = q.shape
     Lk = k.shape[2]
     Dv = v.shape[3] if v.dim() == 4 else -1
@@ -497,7 +507,10 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
             raise ValueError("bad gradient tensor")
         _on_device(t, dev, "gradient")
     nws = bwd_workspace_floats(B, H, Lq)
-    if workspace is None:
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc=True takes no workspace")
+    elif workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.float32, device=q.device)
     elif workspace.dtype != torch.float32 or workspace.numel() < nws:
         raise ValueError("workspace too small")
@@ -509,11 +522,14 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
     bm = block_mask.as_struct()
     bmt = block_mask_t.as_struct()
     scale = default_scale(D) if scale is None else float(scale)
-    _check(load().flex_attn_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-        lse.data_ptr(), dlse.data_ptr() if dlse is not None else None, _DT[q.dtype],
-        B, H, Lq, Lk, D, Dv, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
-        dq.data_ptr() if dq is not None else None, dk.data_ptr(), dv.data_ptr(), _DT[gd],
-        workspace.data_ptr(),
-        _stream_handle(q.device)), "flex_attn_bwd")
+    common = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+              lse.data_ptr(), dlse.data_ptr() if dlse is not None else None, _DT[q.dtype],
+              B, H, Lq, Lk, D, Dv, ctypes.byref(bm), ctypes.byref(bmt), ctypes.byref(sd), scale,
+              dq.data_ptr() if dq is not None else None, dk.data_ptr(), dv.data_ptr(), _DT[gd])
+    if noalloc:
+        _check(load().flex_attn_bwd_noalloc(*common, _stream_handle(q.device)),
+               "flex_attn_bwd_noalloc")
+    else:
+        _check(load().flex_attn_bwd(*common, workspace.data_ptr(), _stream_handle(q.device)),
+               "flex_attn_bwd")
     return dq, dk, dv

@@ -42,13 +42,14 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 6
+#define FLEXATTN_ABI_VERSION 7
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
 #define FLEX_E_INVALID_ARG 1 /* null pointer, negative or mismatched size */
 #define FLEX_E_UNSUPPORTED 2 /* valid but not built: head dim, block size, dtype */
 #define FLEX_E_HIP 3         /* a HIP launch failed */
+#define FLEX_E_SCRATCH_LIMIT 4 /* beyond flex_attn_bwd_noalloc's scratch: 2 B H q_len > FLEX_NOALLOC_SCRATCH_FLOATS */
 
 /* ---- element types ---- */
 #define FLEX_DTYPE_BF16 0
@@ -303,6 +304,28 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const flex_block_mask* bm, const flex_block_mask_t* bmt,
                       const flex_score_desc* score, float scale, void* dq, void* dk,
                       void* dv, int32_t grad_dtype, float* workspace, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * as flex_attn_bwd, with the same arguments and errors, but without the
+ * workspace argument.  The workspace is a file-scope device array of the
+ * library, FLEX_NOALLOC_SCRATCH_FLOATS floats (32 MiB), one copy per GPU,
+ * held until the process ends; the call itself allocates nothing.
+ *   Limit: 2 * B * H * q_len <= FLEX_NOALLOC_SCRATCH_FLOATS (2^22 query rows
+ *   in all); larger calls return FLEX_E_SCRATCH_LIMIT before anything is
+ *   launched.
+ *   Every call on a GPU uses that GPU's one array, so calls whose work
+ *   overlaps on one GPU (concurrent streams, other threads) race on it: the
+ *   caller orders them.  Nothing in the array needs to start at zero (each
+ *   call writes every element it reads first). */
+#define FLEX_NOALLOC_SCRATCH_FLOATS (1 << 23)
+int32_t flex_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                              const void* dout, const float* lse, const float* dlse,
+                              int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
+                              int32_t kv_len, int32_t head_dim, int32_t v_head_dim,
+                              const flex_block_mask* bm, const flex_block_mask_t* bmt,
+                              const flex_score_desc* score, float scale, void* dq, void* dk,
+                              void* dv, int32_t grad_dtype, void* stream);
 
 /* Measurement helper, not part of the attention path: the matrix-unit peak
  * the forward's rate is compared with.  Launches n_workgroups work-groups of
