@@ -160,6 +160,28 @@ __device__ inline void mark_touched(const MaskBuildParams& p, int r0, int r1, in
   __syncthreads();
 }
 
+// Document masks need non-decreasing ids on both sides (then every row sees
+// one run of keys).  Each thread compares one id of each array with the
+// next; a work-group that finds one below its predecessor overwrites every
+// interval with the poison pair (kDocPoisonLo, kDocPoisonHi): empty for the
+// classification below, so no tile is listed, and the forward and backward
+// write NaN for every row and key, so that the broken precondition shows
+// instead of giving plausible wrong numbers.  Runs after doc_bounds_kernel,
+// on the same stream.
+__global__ __launch_bounds__(256) void doc_order_check_kernel(const int32_t* a, int na,
+                                                              const int32_t* b, int nb,
+                                                              int32_t* out, int n_out) {
+  const int t = blockIdx.x * 256 + (int)threadIdx.x;
+  int bad = 0;
+  if (t + 1 < na && a[t] > a[t + 1]) bad = 1;
+  if (t + 1 < nb && b[t] > b[t + 1]) bad = 1;
+  if (!__syncthreads_or(bad)) return;
+  for (int i = (int)threadIdx.x; i < n_out; i += 256) {
+    out[2 * (size_t)i] = kDocPoisonLo;
+    out[2 * (size_t)i + 1] = kDocPoisonHi;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildParams p) {
   __shared__ int scratch[kWaves];
   __shared__ unsigned touched[kChunk / 32];
@@ -300,7 +322,12 @@ hipError_t launch_block_mask_t(const MaskBuildParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(doc_bounds_kernel, dim3((unsigned)((p.kv_len + 255) / 256)), dim3(256), 0,
                        stream, p.kv_doc, p.kv_len, p.q_doc, p.q_len,
                        p.kind == FLEX_MASK_DOCUMENT_CAUSAL ? 1 : 0, 0, p.bounds);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nchk = max(p.q_len, p.kv_len);
+    hipLaunchKernelGGL(doc_order_check_kernel, dim3((unsigned)((nchk + 255) / 256)), dim3(256), 0,
+                       stream, p.q_doc, p.q_len, p.kv_doc, p.kv_len, p.bounds, p.kv_len);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(build_block_mask_t_kernel, dim3(p.n_kb), dim3(kThreads), 0,
@@ -314,7 +341,12 @@ hipError_t launch_block_mask(const MaskBuildParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(doc_bounds_kernel, dim3((unsigned)((p.q_len + 255) / 256)), dim3(256), 0,
                        stream, p.q_doc, p.q_len, p.kv_doc, p.kv_len,
                        p.kind == FLEX_MASK_DOCUMENT_CAUSAL ? 1 : 0, 1, p.bounds);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nchk = max(p.q_len, p.kv_len);
+    hipLaunchKernelGGL(doc_order_check_kernel, dim3((unsigned)((nchk + 255) / 256)), dim3(256), 0,
+                       stream, p.q_doc, p.q_len, p.kv_doc, p.kv_len, p.bounds, p.q_len);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(build_block_mask_kernel, dim3(p.n_qb), dim3(kThreads), 0,

@@ -414,13 +414,18 @@ struct Bf16BwdDq {
 
     // bf16 dq goes through LDS (every wave is past the last step barrier,
     // no load in flight): whole 16-byte pieces over contiguous rows
+    // (document ids out of order: the builder poisoned every interval, and
+    // the row's gradient is NaN)
+    float fq = p.scale;
+    if constexpr (MASK == FLEX_MASK_DOCUMENT)
+      if (fwd::doc_poisoned(lo, hi)) fq = fwd::opaque_nan();
     constexpr bool LDS_DQ = NW * 32 * ROWB <= STAGE + STAGEV;
     if (LDS_DQ && p.grad_bf16 != 0)
       fwd::store_rows_bf16_lds<NE>(buf[0] + wave * 32 * ROWB,
                                    static_cast<char*>(p.dq) + (head_q + (size_t)(q0 + wave * 32)) * ROWB,
-                                   p.q_len - (q0 + wave * 32), acc, p.scale, lane);
+                                   p.q_len - (q0 + wave * 32), acc, fq, lane);
     else if (ok)
-      write_row_t<NE>(p.dq, p.grad_bf16 != 0, head_q + qi, D, g, acc, p.scale);
+      write_row_t<NE>(p.dq, p.grad_bf16 != 0, head_q + qi, D, g, acc, fq);
   }
 };
 
@@ -709,18 +714,23 @@ struct Bf16BwdDkv {
 
     // bf16 dk and dv go through LDS like dq: wave w uses stage buffer w % 2
     // at region w / 2 (every wave is past the last step barrier)
+    // (document ids out of order: the builder poisoned every interval, and
+    // the key's gradients are NaN)
+    float fk = p.scale, fv = 1.0f;
+    if constexpr (MASK == FLEX_MASK_DOCUMENT)
+      if (fwd::doc_poisoned(qlo, qhi)) fk = fv = fwd::opaque_nan();
     constexpr int REG = 32 * (ROWB > ROWBV ? ROWB : ROWBV);
     constexpr bool LDS_DKV = ((NW + 1) / 2) * REG <= STAGEB;
     if (LDS_DKV && p.grad_bf16 != 0) {
       lds_t* reg = ((wave & 1) ? buf[1] : buf[0]) + (wave >> 1) * REG;
       const int k0 = kb * KB + wave * 32;
       fwd::store_rows_bf16_lds<NE>(reg, static_cast<char*>(p.dk) + (head_kv + (size_t)k0) * ROWB,
-                                   p.kv_len - k0, dk, p.scale, lane);
+                                   p.kv_len - k0, dk, fk, lane);
       fwd::store_rows_bf16_lds<NEV>(reg, static_cast<char*>(p.dv) + (head_kv + (size_t)k0) * ROWBV,
-                                    p.kv_len - k0, dv, 1.0f, lane);
+                                    p.kv_len - k0, dv, fv, lane);
     } else if (kok) {
-      write_row_t<NE>(p.dk, p.grad_bf16 != 0, head_kv + kk, D, g, dk, p.scale);
-      write_row_t<NEV>(p.dv, p.grad_bf16 != 0, head_kv + kk, DV, g, dv, 1.0f);
+      write_row_t<NE>(p.dk, p.grad_bf16 != 0, head_kv + kk, D, g, dk, fk);
+      write_row_t<NEV>(p.dv, p.grad_bf16 != 0, head_kv + kk, DV, g, dv, fv);
     }
   }
 };

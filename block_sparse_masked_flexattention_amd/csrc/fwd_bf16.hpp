@@ -593,7 +593,11 @@ struct Bf16Fwd {
     for (int c = 0; c < NQ; ++c) {
       const float l_tot = l_run[c] + xor32(l_run[c]);
       const bool live = p.safe_rows || l_tot > 0.f;
-      const float inv = live ? 1.0f / l_tot : 0.f;
+      float inv = live ? 1.0f / l_tot : 0.f;
+      // document ids out of order: the builder poisoned every interval
+      bool poison = false;
+      if constexpr (MASK == FLEX_MASK_DOCUMENT) poison = doc_poisoned(lo[c], hi[c]);
+      if (poison) inv = opaque_nan();
       if (lds_out)
         store_rows_bf16_lds<NE>(buf[0] + wave * 32 * OROW,
                                 static_cast<char*>(p.out) + (head_q + (size_t)(q0 + wave * 32)) * OROW,
@@ -601,7 +605,8 @@ struct Bf16Fwd {
       if (qi[c] < p.q_len) {
         if (!lds_out) write_out_row<NE>(p, head_q + qi[c], DV, g, o[c], inv);
         if (p.lse != nullptr && g == 0)
-          p.lse[head_q + qi[c]] = live ? (m_run[c] + log2f(l_tot)) * kLn2 : -INFINITY;
+          p.lse[head_q + qi[c]] = poison ? opaque_nan()
+                                         : live ? (m_run[c] + log2f(l_tot)) * kLn2 : -INFINITY;
         if constexpr (XMAX) {
           if (p.max_out != nullptr && g == 0) p.max_out[head_q + qi[c]] = m_run[c] * kLn2;
         }

@@ -119,6 +119,22 @@ __device__ inline void row_interval(const P& p, int qi, int& lo, int& hi) {
   }
 }
 
+// Document masks: true for the interval pair (kDocPoisonLo, kDocPoisonHi)
+// the builder writes when the ids are not non-decreasing; the forward and
+// backward write NaN for such a row or key.
+__device__ inline bool doc_poisoned(int lo, int hi) {
+  return lo == kDocPoisonLo && hi == kDocPoisonHi;
+}
+
+// A quiet NaN the compiler cannot see as one: the library is built with
+// -fno-honor-nans, under which a NaN constant lets it fold the arithmetic
+// that carries it.
+__device__ inline float opaque_nan() {
+  float x;
+  asm volatile("v_mov_b32 %0, 0x7fc00000" : "=v"(x));
+  return x;
+}
+
 // Masks whose rows' intervals can start after key 0: partial tiles test both
 // ends.
 template <int MASK>

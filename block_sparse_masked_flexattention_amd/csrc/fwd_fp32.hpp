@@ -220,11 +220,16 @@ struct Fp32Fwd {
     // the running max is exact here, so the row max is m_run (base 2)
     const float l_tot = l_run + xor32(l_run);
     const bool live = p.safe_rows || l_tot > 0.f;
-    const float inv = live ? 1.0f / l_tot : 0.f;
+    float inv = live ? 1.0f / l_tot : 0.f;
+    // document ids out of order: the builder poisoned every interval
+    bool poison = false;
+    if constexpr (MASK == FLEX_MASK_DOCUMENT) poison = doc_poisoned(lo, hi);
+    if (poison) inv = opaque_nan();
     if (qi < p.q_len) {
       write_out_row<NE>(p, head_q + qi, D, g, o, inv);
       if (p.lse != nullptr && g == 0)
-        p.lse[head_q + qi] = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        p.lse[head_q + qi] = poison ? opaque_nan()
+                                    : live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
       if (p.max_out != nullptr && g == 0) p.max_out[head_q + qi] = m_run * kLn2;
     }
   }

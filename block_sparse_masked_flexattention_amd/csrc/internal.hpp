@@ -9,6 +9,12 @@
 
 namespace flexattn {
 
+// Document masks: the interval pair the builder writes for every row (and
+// every key) when the ids are not non-decreasing.  Empty for the tile
+// classification (first > last).
+constexpr int kDocPoisonLo = 0x7fffffff;
+constexpr int kDocPoisonHi = -0x7fffffff - 1;
+
 // Everything the forward kernel reads, passed by value as the kernel argument.
 struct FwdParams {
   const void* q;

@@ -199,8 +199,13 @@ int32_t flex_attn_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t q_block
  *   order, then every other kv-block in ascending order.
  *   row_bounds: DOCUMENT*: device int32 [2 * q_len], receives each query's
  *   visible key interval (pass it on in flex_block_mask.row_bounds); may be
- *   NULL for the other kinds.  The id arrays are read on the device: ids that
- *   are not non-decreasing give wrong intervals, never out-of-bounds access.
+ *   NULL for the other kinds.  The id arrays are read on the device and
+ *   checked there: if either array has an id below its predecessor, every
+ *   query's interval is set to the empty pair (INT32_MAX, INT32_MIN), no
+ *   kv-block is listed, and the forward writes NaN to every output row and
+ *   log-sum-exp of the call (the backward NaN to every dq, dk and dv row),
+ *   so the broken precondition shows in the results.  No error code: the
+ *   check runs on the stream, after the call has returned.
  * Errors: FLEX_E_INVALID_ARG (null pointer with a non-empty output, bad sizes,
  * bad mask parameters), FLEX_E_UNSUPPORTED (unknown mask kind), FLEX_E_HIP. */
 int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
@@ -220,7 +225,10 @@ int32_t flex_attn_build_block_mask(const flex_mask_desc* mask, int32_t q_len,
  *   others ascending).
  *   col_bounds: DOCUMENT*: device int32 [2 * kv_len], receives the interval
  *   of queries that see each key (pass it on in flex_block_mask_t.col_bounds);
- *   may be NULL for the other kinds.
+ *   may be NULL for the other kinds.  Ids out of order are caught as in
+ *   flex_attn_build_block_mask: every key's interval becomes the empty pair
+ *   (INT32_MAX, INT32_MIN), no q-block is listed, and the backward writes
+ *   NaN to every dk and dv row.
  * Errors: as flex_attn_build_block_mask. */
 int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
                                      int32_t kv_len, int32_t q_block,

@@ -178,3 +178,52 @@ def test_backward_parity(over):
     cfg2 = dict(cfg, mask=mask)
     ref = oracle_bwd(cfg2, q, k, v, dout, dlse)
     check(got, ref, torch.float32, "document bwd %s" % over)
+
+
+UNSORTED_CASES = [
+    # (q ids, kv ids): a step down in the query ids, in the key ids, and one
+    # across the check kernel's 256-thread boundary (positions 255 -> 256)
+    (np.r_[[0] * 100, [2] * 60, [1] * 40, [3] * 100], None),
+    (np.r_[[0] * 150, [1] * 150], np.r_[[0] * 120, [1] * 60, [0] * 120]),
+    (np.r_[[0] * 256, [1] * 344], np.r_[[0] * 100, [1] * 156, [0] * 344]),
+]
+
+
+@pytest.mark.parametrize("qids,kvids", UNSORTED_CASES, ids=["q-step", "kv-step", "kv-boundary"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_unsorted_ids_give_nan(qids, kvids, dtype):
+    """Ids that are not non-decreasing break the builder's precondition: it
+    lists no tile, every bounds pair is (INT32_MAX, INT32_MIN), and the
+    forward and backward write NaN everywhere instead of plausible numbers."""
+    q_doc = torch.from_numpy(np.asarray(qids, np.int32))
+    kv_doc = q_doc if kvids is None else torch.from_numpy(np.asarray(kvids, np.int32))
+    L = int(q_doc.numel())
+    assert kv_doc.numel() == L
+    cfg = workload("document_causal", B=1, H=2, q_len=L, kv_len=L, q_block=64, kv_block=64,
+                   dtype="bf16" if dtype == torch.bfloat16 else "fp32")
+    for kind in ("document", "document_causal"):
+        print("case", kind, dtype, L, flush=True)
+        mask = _dev(_mask(kind, q_doc, kv_doc))
+        bm = fa.build_block_mask(mask, L, L, 64, 64, device=DEV)
+        bmt = fa.build_block_mask_t(mask, L, L, 64, 64, device=DEV)
+        torch.cuda.synchronize()
+        for arr in (bm.kv_num_blocks, bm.full_kv_num_blocks, bmt.q_num_blocks, bmt.full_q_num_blocks):
+            assert int(arr.abs().sum()) == 0
+        for b in (bm.row_bounds, bmt.col_bounds):
+            b = b.cpu().view(-1, 2)
+            assert bool((b[:, 0] == 2**31 - 1).all()) and bool((b[:, 1] == -2**31).all())
+        q, k, v = make_inputs(cfg)
+        qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+        for out_dtype in (torch.float32, torch.bfloat16):
+            out, lse = fa.fwd(qd, kd, vd, bm, None, cfg["scale"], out_dtype=out_dtype,
+                              return_lse=True)
+            torch.cuda.synchronize()
+            assert bool(out.float().isnan().all()) and bool(lse.isnan().all())
+        if dtype != torch.bfloat16:
+            continue
+        dout, dlse = make_grad_inputs(cfg, with_dlse=True)
+        dq, dk, dv = fa.bwd(qd, kd, vd, out, dout.to(DEV), lse, bm, bmt, None, cfg["scale"],
+                            dlse=dlse.to(DEV))
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            assert bool(g.float().isnan().all())
