@@ -199,6 +199,50 @@ struct Bf16Fwd {
         vro[e] = STAGE + r0 * ROWBV + (((8 * e + 4 * u + (j & 3)) ^ vswz(r0)) << 3);
     }
 
+    // ---- tile list (read first: the first step's loads wait for it, the
+    // Q loads below do not): partial tiles, then full tiles, each list walked from
+    // its last entry down.  Lists are ascending, so under causal-type masks
+    // the nearest keys (the diagonal, the largest scores under a decaying
+    // bias) come first, which keeps the lagging offset from being raised
+    // again later; and under a sliding window every wave meets its first
+    // visible keys in the same step, so the slow-path blocks of the four
+    // waves overlap instead of following one another. ----
+    const int nk = p.n_kb;
+    int np_raw = p.kv_num[qb], nf_raw = p.fkv_num[qb];
+    asm volatile("" : "+s"(np_raw), "+s"(nf_raw));  // both loads out before either wait
+    const int np = min(max(np_raw, 0), nk);
+    const int nf = min(max(nf_raw, 0), nk);
+    const int ntiles = np + nf;
+    const int nsteps = ntiles * SPT;
+    const int32_t* prow = p.kv_idx + (size_t)qb * nk;
+    const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
+    // Tile indices 64 at a time: lane i of `win` holds the kv-block of tile
+    // win_base + i, lane i of `win_nx` that of tile win_base + 64 + i; a
+    // tile's index is then one v_readlane.  The next window is loaded 64
+    // tiles ahead of its use.
+    auto load_window = [&](int base) {  // raw values; clamped when read
+      // (each list from its last entry down; one load per lane from inside
+      // the index rows whatever the count, with no branch around it, so
+      // that the wait for it can leave the Q loads issued after it in flight)
+      // With no kv-blocks at all the index rows are empty: the lane reads
+      // the q-block's count instead (the value is never used).
+      const int t = max(min(base + lane, ntiles - 1), 0);
+      const bool in_p = t < np;
+      const int j = in_p ? np - 1 - t : ntiles - 1 - t;  // entry of its list
+      const int32_t* src = (in_p ? prow : frow) + (p.contig ? 0 : max(j, 0));
+      const int v = *(nk > 0 ? src : p.kv_num + qb);
+      return p.contig ? v + j : v;  // a contiguous list is first, first + 1, ...
+    };
+    int win_base = 0;
+    int win = load_window(0);
+    int win_nx = load_window(64);
+    auto tile_kb = [&](int t) {  // t in [win_base, win_base + 128)
+      const int i = t - win_base;
+      const int v = i < 64 ? __builtin_amdgcn_readlane(win, i)
+                           : __builtin_amdgcn_readlane(win_nx, i - 64);
+      return min(max(v, 0), nk - 1);
+    };
+
     // ---- Q fragments: B operand of S^T = K Q^T ----
     // q times -1 (negative scale) or scale * log2 e (PRESCALE_QK); times 1
     // otherwise.  Both signs and 1 are exact in bf16.
@@ -208,13 +252,12 @@ struct Bf16Fwd {
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
       qi[c] = q0 + (wave * NQ + c) * 32 + lq;
-      const bool ok = qi[c] < p.q_len;
+      // rows past the end load the last row (zeroed below): no branch
+      // around the loads
+      const int qr = min(qi[c], p.q_len - 1);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        qf[c][t] = ok ? ld_global16(qg + (size_t)qi[c] * ROWB + (2 * t + g) * 16)
-                      : u32x4{0, 0, 0, 0};
-        qf[c][t] = scale_bf16x8(qf[c][t], qmul);
-      }
+      for (int t = 0; t < D / 16; ++t)
+        qf[c][t] = ld_global16(qg + (size_t)qr * ROWB + (2 * t + g) * 16);
     }
 
     // ---- per-row visible key interval [lo, hi] ----
@@ -240,44 +283,6 @@ struct Bf16Fwd {
       bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * kLn2);
       bias_u16 = 16.0f * bias_u;
     }
-
-    // ---- tile list: partial tiles, then full tiles, each list walked from
-    // its last entry down.  Lists are ascending, so under causal-type masks
-    // the nearest keys (the diagonal, the largest scores under a decaying
-    // bias) come first, which keeps the lagging offset from being raised
-    // again later; and under a sliding window every wave meets its first
-    // visible keys in the same step, so the slow-path blocks of the four
-    // waves overlap instead of following one another. ----
-    const int nk = p.n_kb;
-    const int np = min(max(p.kv_num[qb], 0), nk);
-    const int nf = min(max(p.fkv_num[qb], 0), nk);
-    const int ntiles = np + nf;
-    const int nsteps = ntiles * SPT;
-    const int32_t* prow = p.kv_idx + (size_t)qb * nk;
-    const int32_t* frow = p.fkv_idx + (size_t)qb * nk;
-    // Tile indices 64 at a time: lane i of `win` holds the kv-block of tile
-    // win_base + i, lane i of `win_nx` that of tile win_base + 64 + i; a
-    // tile's index is then one v_readlane.  The next window is loaded 64
-    // tiles ahead of its use.
-    auto load_window = [&](int base) {  // raw values; clamped when read
-      const int t = min(base + lane, ntiles - 1);
-      int v = 0;
-      if (t >= 0) {
-        // (each list from its last entry down)
-        if (p.contig) v = t < np ? prow[0] + (np - 1 - t) : frow[0] + (ntiles - 1 - t);
-        else v = t < np ? prow[np - 1 - t] : frow[ntiles - 1 - t];
-      }
-      return v;
-    };
-    int win_base = 0;
-    int win = load_window(0);
-    int win_nx = ntiles > 64 ? load_window(64) : 0;
-    auto tile_kb = [&](int t) {  // t in [win_base, win_base + 128)
-      const int i = t - win_base;
-      const int v = i < 64 ? __builtin_amdgcn_readlane(win, i)
-                           : __builtin_amdgcn_readlane(win_nx, i - 64);
-      return min(max(v, 0), nk - 1);
-    };
 
     // Load step m into a stage buffer: K and V, 16 bytes per lane per
     // instruction straight into LDS.  The instruction's LDS slot for lane i
@@ -561,8 +566,18 @@ struct Bf16Fwd {
       step_barrier();
     };
 
-    // prologue: step 0 in flight, then wait for it
+    // prologue: step 0 in flight, then wait for it (the Q scaling, when
+    // there is one, runs meanwhile)
     if (nsteps > 0) dma(buf[0], 0);
+    if (qmul != 1.0f || q_ragged) {
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) {
+        const bool ok = qi[c] < p.q_len;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t)
+          qf[c][t] = ok ? scale_bf16x8(qf[c][t], qmul) : u32x4{0, 0, 0, 0};
+      }
+    }
     step_barrier();
     // pairs of steps, straight-line, then the remainder; the first step is
     // peeled off and takes the exact update: a row's first visible keys cost

@@ -108,11 +108,12 @@ __device__ inline void row_interval(const P& p, int qi, int& lo, int& hi) {
     hi = min(hi, qi <= p.prefix ? max(p.prefix, qi) : qi);
   } else if constexpr (MASK == FLEX_MASK_DOCUMENT) {
     // both document kinds: the builder's per-row interval (causal cut
-    // included); rows past the end see nothing
-    if (qi < p.q_len) {
-      lo = p.bounds[2 * (size_t)qi];
-      hi = p.bounds[2 * (size_t)qi + 1];
-    } else {
+    // included); rows past the end see nothing (they read the last row's
+    // pair, with no branch around the loads, and drop it)
+    const size_t qc = (size_t)min(qi, p.q_len - 1);
+    lo = p.bounds[2 * qc];
+    hi = p.bounds[2 * qc + 1];
+    if (qi >= p.q_len) {
       lo = 1;
       hi = 0;
     }
