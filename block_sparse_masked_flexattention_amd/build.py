@@ -27,13 +27,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # amdgpu-mfma-vgpr-form: keep matrix-instruction accumulators in ordinary
 # VGPRs; the softmax reads every score and rescales the output accumulator,
 # and accumulators parked in AGPRs would cost a copy each way.
-# -fno-honor-nans: lets fmaxf become a bare v_max/v_max3 (no NaN-quieting
-# copy of each operand); inputs holding NaN give unspecified outputs.
-# Infinities are still honoured (masked scores are -inf).
+# -fno-honor-nans, device pass only: lets fmaxf become a bare v_max/v_max3
+# (no NaN-quieting copy of each operand); inputs holding NaN give
+# unspecified outputs.  Infinities are still honoured (masked scores are
+# -inf).  The host pass honours NaNs: its argument checks test for them.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Xarch_device", "-fno-honor-nans",
     "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]

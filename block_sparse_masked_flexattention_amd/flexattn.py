@@ -16,7 +16,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libflexattn.so")
+# FLEXATTN_LIB: another build of the same library (for instance one with
+# host-side sanitizers)
+LIB_PATH = os.environ.get("FLEXATTN_LIB") or os.path.join(_HERE, "libflexattn.so")
 
 FLEX_OK, FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP, FLEX_E_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 NOALLOC_SCRATCH_FLOATS = 1 << 23

@@ -22,7 +22,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _OUT_DIR = os.path.join(_HERE, "_build")
-_LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
+# FLEXATTN_ORACLE_LIB: another build of oracle.c (for instance one with
+# sanitizers), loaded as it is
+_LIB_ENV = os.environ.get("FLEXATTN_ORACLE_LIB")
+_LIB_PATH = _LIB_ENV or os.path.join(_OUT_DIR, "liboracle.so")
 
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
@@ -49,7 +52,7 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH):
+        if not os.path.exists(_LIB_PATH) and not _LIB_ENV:
             build(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         i64, i32p, f32p, f64p, i64p = (
