@@ -2,12 +2,20 @@
 // include/flexattn.h).  Host-side validation, then one kernel launch on the
 // caller's stream.  Nothing here allocates, synchronises or keeps state.
 #include <math.h>
+#include <stdlib.h>
 
 #include "internal.hpp"
 
 using namespace flexattn;
 
 namespace {
+
+// FLEXATTN_DEBUG_LDS_POISON set to anything but "0": read on every call, so
+// that a test can switch it per call.
+int32_t lds_poison_requested() {
+  const char* e = getenv("FLEXATTN_DEBUG_LDS_POISON");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0') ? 1 : 0;
+}
 
 bool mask_ok(const flex_mask_desc& m, int32_t* err) {
   switch (m.kind) {
@@ -248,6 +256,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   }
   p.safe_rows = o.rows_guaranteed_safe != 0 ? 1 : 0;
   p.contig = o.blocks_are_contiguous != 0 ? 1 : 0;
+  p.lds_poison = lds_poison_requested();
   p.bounds = bm->row_bounds;
   const int variant = (o.use_subtiling != 0 ? kFwdSubtile : 0) | (max_out ? kFwdExactMax : 0);
   return launch_fwd(p, in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block,

@@ -127,6 +127,7 @@ struct Bf16Fwd {
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
   static_assert(NDMAV * 64 * NW == KS * CPRV, "step split (V)");
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert((STAGE + STAGEV) % (16 * NT) == 0, "stage fill");
   static_assert(DV == 64 || DV == 128, "value head dim");
 
   // K: row m, 16-byte chunk c at chunk c ^ kswz(m)
@@ -159,6 +160,24 @@ struct Bf16Fwd {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+  }
+
+  // Debugging (lds_poison): fill a stage buffer with NaN (all-ones bf16),
+  // then the work-group barrier, so that the fill lands before the loads
+  // that refill the buffer are issued.  A step that read a buffer before its
+  // loads landed, or after the next step's loads began to overwrite it,
+  // would then see NaN instead of plausible stale values.
+  // (The thread index and the fill value are rebuilt here behind empty asm
+  // statements, so that nothing of this rarely taken path is hoisted into
+  // registers that stay live through the step loop.)
+  __device__ static inline void poison_stage(lds_t* b) {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    unsigned ones = ~0u;
+    asm volatile("" : "+v"(ones));
+#pragma unroll
+    for (int i = 0; i < (STAGE + STAGEV) / (16 * NT); ++i)
+      FLEXATTN_LDS(u32x4, b + 16 * (t + i * NT)) = u32x4{ones, ones, ones, ones};
   }
 
   __device__ static void run(const FwdParams& p) {
@@ -424,6 +443,10 @@ struct Bf16Fwd {
       const int kv0 = kb * KB + part * KS;
       // a listed-full tile at a ragged edge is still handled as partial
       const bool partial = t < np || q_ragged || kb * KB + KB > p.kv_len;
+      if (p.lds_poison) {  // (every wave is past the barrier that ended step n - 1)
+        poison_stage(buf[B ^ 1]);
+        __syncthreads();
+      }
       if (n + 1 < nsteps) dma(buf[B ^ 1], n + 1);
 
 #pragma unroll
@@ -568,6 +591,11 @@ struct Bf16Fwd {
 
     // prologue: step 0 in flight, then wait for it (the Q scaling, when
     // there is one, runs meanwhile)
+    if (p.lds_poison) {
+      poison_stage(buf[0]);
+      poison_stage(buf[1]);
+      __syncthreads();
+    }
     if (nsteps > 0) dma(buf[0], 0);
     if (qmul != 1.0f || q_ragged) {
 #pragma unroll

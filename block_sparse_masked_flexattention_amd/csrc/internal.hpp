@@ -40,6 +40,9 @@ struct FwdParams {
   int32_t safe_rows;  // ROWS_GUARANTEED_SAFE: no fully masked-row guards
   int32_t contig;     // BLOCKS_ARE_CONTIGUOUS: list n is first + n
   const int32_t* bounds;  // document masks: [2 * q_len] visible key interval per row
+  // debugging (FLEXATTN_DEBUG_LDS_POISON): the bf16 kernel fills each K/V
+  // stage buffer with NaN before its next loads are issued
+  int32_t lds_poison;
 };
 
 // Backward: gradients of q, k and v.  Both block masks are the forward's

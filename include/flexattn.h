@@ -261,6 +261,13 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
  * {(64, 64), (128, 64), (128, 128)}; any mask kind and score kind; out_dtype
  * BF16 or FP32.  q_len, kv_len >= 0 (ragged last
  * blocks are fine), B, H >= 0, B * H * n_q_blocks < 2^31.
+ * Debugging: with the environment variable FLEXATTN_DEBUG_LDS_POISON set
+ * (to anything but "0"; read on every call) the BF16-input forward fills
+ * each K/V staging buffer in LDS with NaN, behind a work-group barrier,
+ * before the loads that refill it are issued.  A read of a buffer before its
+ * loads have landed, or after the next loads began to overwrite it, then
+ * gives NaN output instead of plausible wrong values.  The results are
+ * otherwise bit-identical; the calls are slower.
  * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED, FLEX_E_HIP. */
 int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
                       int32_t in_dtype, int32_t B, int32_t H, int32_t q_len,
