@@ -190,13 +190,18 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   if (!mask_ok(bm->mask, &err)) return err;
   int32_t score_kind = FLEX_SCORE_IDENTITY;
   float bias_max = 0.f;
+  const float* slopes = nullptr;
   if (score) {
     score_kind = score->kind;
     if (score_kind != FLEX_SCORE_IDENTITY && score_kind != FLEX_SCORE_REL_BIAS)
       return FLEX_E_UNSUPPORTED;
     if (score_kind == FLEX_SCORE_REL_BIAS) {
-      if (score->num_heads != H || !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      if (score->num_heads != H) return FLEX_E_INVALID_ARG;
+      if (score->slopes == nullptr && !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      if (score->slopes != nullptr && (reinterpret_cast<uintptr_t>(score->slopes) & 3) != 0)
+        return FLEX_E_INVALID_ARG;
       bias_max = score->bias_max;
+      slopes = score->slopes;
     }
   }
   if (!fwd_supported(in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block))
@@ -244,6 +249,7 @@ int32_t flex_attn_fwd(const void* q, const void* k, const void* v,
   p.c1 = fabsf(scale) * 1.44269504088896340736f;
   p.neg_q = scale < 0.f ? 1 : 0;
   p.bias_max = bias_max;
+  p.slopes = slopes;
   p.out_bf16 = out_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
   // PRESCALE_QK: q carries scale * log2 e (sign included); scores come out
   // of the product in base-2 units
@@ -299,13 +305,18 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   if (!mask_ok(bm->mask, &err)) return err;
   int32_t score_kind = FLEX_SCORE_IDENTITY;
   float bias_max = 0.f;
+  const float* slopes = nullptr;
   if (score) {
     score_kind = score->kind;
     if (score_kind != FLEX_SCORE_IDENTITY && score_kind != FLEX_SCORE_REL_BIAS)
       return FLEX_E_UNSUPPORTED;
     if (score_kind == FLEX_SCORE_REL_BIAS) {
-      if (score->num_heads != H || !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      if (score->num_heads != H) return FLEX_E_INVALID_ARG;
+      if (score->slopes == nullptr && !isfinite(score->bias_max)) return FLEX_E_INVALID_ARG;
+      if (score->slopes != nullptr && (reinterpret_cast<uintptr_t>(score->slopes) & 3) != 0)
+        return FLEX_E_INVALID_ARG;
       bias_max = score->bias_max;
+      slopes = score->slopes;
     }
   }
   if (!bwd_supported(in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block))
@@ -372,6 +383,7 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   p.inv_abs_scale = 1.0f / fabsf(scale);
   p.neg = scale < 0.f ? 1 : 0;
   p.bias_max = bias_max;
+  p.slopes = slopes;
   p.grad_bf16 = grad_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
   return launch_bwd(p, head_dim, v_head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
                     score_kind, static_cast<hipStream_t>(stream)) == hipSuccess

@@ -251,7 +251,7 @@ struct Bf16BwdDq {
     const float c1 = p.c1;
     float bias_u = 0.f, bias_u16 = 0.f;
     if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
-      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * fwd::kLn2);
+      bias_u = -fwd::head_slope(p, h) / (p.c1 * fwd::kLn2);
       bias_u16 = 16.0f * bias_u;
     }
 
@@ -502,7 +502,7 @@ struct Bf16BwdDkv {
     const float c1 = p.c1;
     float bias_u = 0.f, bias_u16 = 0.f;
     if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
-      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * fwd::kLn2);
+      bias_u = -fwd::head_slope(p, h) / (p.c1 * fwd::kLn2);
       bias_u16 = 16.0f * bias_u;
     }
 

@@ -219,18 +219,21 @@ struct Bf16Fwd {
     }
 
     // ---- tile list (read first: the first step's loads wait for it, the
-    // Q loads below do not): partial tiles, then full tiles, each list walked from
-    // its last entry down.  Lists are ascending, so under causal-type masks
-    // the nearest keys (the diagonal, the largest scores under a decaying
-    // bias) come first, which keeps the lagging offset from being raised
-    // again later; and under a sliding window every wave meets its first
-    // visible keys in the same step, so the slow-path blocks of the four
-    // waves overlap instead of following one another. ----
+    // Q loads below do not): partial tiles, then full tiles, each list walked
+    // from its last entry down.  Lists are ascending, so under causal-type
+    // masks the nearest keys (the diagonal, the largest scores under a
+    // decaying bias) come first, which keeps the lagging offset from being
+    // raised again later; and under a sliding window every wave meets its
+    // first visible keys in the same step, so the slow-path blocks of the
+    // four waves overlap instead of following one another.  (Walking the
+    // full tiles upwards instead, so that the q-blocks of a head that run
+    // together would read key block 0 first at about the same time, measured
+    // 1.5 times the HBM reads on the 4096-long prefix workload: descending,
+    // q-block i + 1 reads each tile two steps before q-block i does, a short
+    // and steady reuse distance.) ----
     const int nk = p.n_kb;
-    int np_raw = p.kv_num[qb], nf_raw = p.fkv_num[qb];
-    asm volatile("" : "+s"(np_raw), "+s"(nf_raw));  // both loads out before either wait
-    const int np = min(max(np_raw, 0), nk);
-    const int nf = min(max(nf_raw, 0), nk);
+    const int np = min(max(p.kv_num[qb], 0), nk);
+    const int nf = min(max(p.fkv_num[qb], 0), nk);
     const int ntiles = np + nf;
     const int nsteps = ntiles * SPT;
     const int32_t* prow = p.kv_idx + (size_t)qb * nk;
@@ -240,11 +243,11 @@ struct Bf16Fwd {
     // tile's index is then one v_readlane.  The next window is loaded 64
     // tiles ahead of its use.
     auto load_window = [&](int base) {  // raw values; clamped when read
-      // (each list from its last entry down; one load per lane from inside
-      // the index rows whatever the count, with no branch around it, so
-      // that the wait for it can leave the Q loads issued after it in flight)
-      // With no kv-blocks at all the index rows are empty: the lane reads
-      // the q-block's count instead (the value is never used).
+      // (one load per lane from inside the index rows whatever the count,
+      // with no branch around it, so that the wait for it can leave the Q
+      // loads issued after it in flight.  With no kv-blocks at all the index
+      // rows are empty: the lane reads the q-block's count instead, a value
+      // never used.)
       const int t = max(min(base + lane, ntiles - 1), 0);
       const bool in_p = t < np;
       const int j = in_p ? np - 1 - t : ntiles - 1 - t;  // entry of its list
@@ -299,7 +302,7 @@ struct Bf16Fwd {
     // of q - kv.
     float bias_u = 0.f, bias_u16 = 0.f;
     if constexpr (SCORE == FLEX_SCORE_REL_BIAS) {
-      bias_u = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) / (p.c1 * kLn2);
+      bias_u = -head_slope(p, h) / (p.c1 * kLn2);
       bias_u16 = 16.0f * bias_u;
     }
 

@@ -120,6 +120,13 @@ __device__ inline void row_interval(const P& p, int qi, int& lo, int& hi) {
   }
 }
 
+// REL_BIAS slope of head h: from the caller's per-head table when there is
+// one (a score modification that closes over a tensor), else the formula.
+template <typename P>
+__device__ inline float head_slope(const P& p, int h) {
+  return p.slopes != nullptr ? p.slopes[h] : exp2f(-p.bias_max * (float)(h + 1) / (float)p.H);
+}
+
 // Document masks: true for the interval pair (kDocPoisonLo, kDocPoisonHi)
 // the builder writes when the ids are not non-decreasing; the forward and
 // backward write NaN for such a row or key.

@@ -63,7 +63,7 @@ struct Fp32Fwd {
     row_interval<MASK>(p, qi, lo, hi);
     float nsl2 = 0.f;
     if constexpr (SCORE == FLEX_SCORE_REL_BIAS)
-      nsl2 = -exp2f(-p.bias_max * (float)(h + 1) / (float)p.H) * kLog2e;
+      nsl2 = -head_slope(p, h) * kLog2e;
 
     const int nk = p.n_kb;
     const int np = min(max(p.kv_num[qb], 0), nk);

@@ -32,6 +32,7 @@ struct FwdParams {
   float c1;        // |scale| * log2(e): scores are kept in base-2 units
   int32_t neg_q;   // scale < 0: q is negated on load so c1 stays positive
   float bias_max;  // REL_BIAS: slope_h = 2^(-bias_max * (h + 1) / H)
+  const float* slopes;  // REL_BIAS: slope_h = slopes[h] instead (may be null)
   int32_t out_bf16;
   // PRESCALE_QK: q is multiplied by qscale (= scale * log2 e) and rounded to
   // the input type on load; c1 is then 1 and neg_q 0
@@ -76,6 +77,7 @@ struct BwdParams {
   float inv_abs_scale;
   int32_t neg;       // scale < 0: the sign goes onto q (dq kernel) or k (dk/dv kernel)
   float bias_max;
+  const float* slopes;
   int32_t grad_bf16;
 };
 

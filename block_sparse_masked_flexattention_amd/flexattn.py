@@ -26,7 +26,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 MASK_KINDS = {"noop": 0, "causal": 1, "sliding_window": 2, "prefix_causal": 3,
               "document": 4, "document_causal": 5}
 SCORE_KINDS = {"identity": 0, "rel_bias": 1}
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # the functions include/flexattn.h declares
 EXPORTED = (
@@ -75,7 +75,22 @@ class BlockMaskTStruct(ctypes.Structure):
 
 class ScoreDesc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("num_heads", ctypes.c_int32),
-                ("bias_max", ctypes.c_float)]
+                ("bias_max", ctypes.c_float), ("slopes", ctypes.c_void_p)]
+
+
+def score_desc(sc: dict | None, H: int, dev) -> ScoreDesc:
+    """The score dict as the ABI struct: {"kind": "identity"} or
+    {"kind": "rel_bias", "bias_max": 8.0} or {"kind": "rel_bias", "slopes": t}
+    with t a float32 [H] tensor on the call's device (a per-head slope table,
+    read by the kernels)."""
+    sc = sc or {"kind": "identity"}
+    slopes = sc.get("slopes")
+    ptr = None
+    if slopes is not None:
+        _on_device(slopes, dev, "slopes", torch.float32, (H,))
+        ptr = slopes.data_ptr()
+    return ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
+                     float(sc.get("bias_max", 8.0)), ptr)
 
 
 class FwdOptions(ctypes.Structure):
@@ -350,9 +365,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: BlockMask
         max_out = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     if max_out is not None:
         _on_device(max_out, dev, "max_out", torch.float32, (B, H, Lq))
-    sc = score or {"kind": "identity"}
-    sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
-                   float(sc.get("bias_max", 8.0)))
+    sd = score_desc(score, H, dev)
     opt = FwdOptions(int(bool(use_subtiling)), int(bool(prescale_qk)),
                      int(bool(rows_guaranteed_safe)), int(bool(blocks_are_contiguous)))
     bm = block_mask.as_struct()
@@ -518,9 +531,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         raise ValueError("workspace too small")
     else:
         _on_device(workspace, dev, "workspace", torch.float32)
-    sc = score or {"kind": "identity"}
-    sd = ScoreDesc(SCORE_KINDS[sc["kind"]], int(sc.get("num_heads", H)),
-                   float(sc.get("bias_max", 8.0)))
+    sd = score_desc(score, H, dev)
     bm = block_mask.as_struct()
     bmt = block_mask_t.as_struct()
     scale = default_scale(D) if scale is None else float(scale)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FLEXATTN_ABI_VERSION 7
+#define FLEXATTN_ABI_VERSION 8
 
 /* ---- status codes ---- */
 #define FLEX_OK 0
@@ -91,14 +91,23 @@ typedef struct flex_mask_desc {
 /* ---- score modifications (score_mod), applied to the SCALED score s ----
  *   IDENTITY  s
  *   REL_BIAS  s - slope_h * (i - j),  slope_h = 2^(-bias_max * (h + 1) / H),
- *             h the head index, H = num_heads (an ALiBi-style bias). */
+ *             h the head index, H = num_heads (an ALiBi-style bias); or,
+ *             with a slope table, slope_h = slopes[h]: a score_mod that
+ *             closes over a tensor (what the op's score_mod_other_buffers
+ *             slot in the subtiling page's test hunks carries).  The table
+ *             is read, never differentiated: the backward gives no gradient
+ *             for it. */
 #define FLEX_SCORE_IDENTITY 0
 #define FLEX_SCORE_REL_BIAS 1
 
 typedef struct flex_score_desc {
   int32_t kind;      /* FLEX_SCORE_* */
   int32_t num_heads; /* REL_BIAS: H in the slope formula; must equal the call's H */
-  float bias_max;    /* REL_BIAS: 8 for the usual ALiBi slopes; finite */
+  float bias_max;    /* REL_BIAS without a table: 8 for the usual ALiBi slopes; finite */
+  const float* slopes; /* REL_BIAS: NULL, or device fp32 [num_heads], 4-byte aligned,
+                          finite values (any sign), read by the kernels; bias_max
+                          is then ignored.  The caller keeps it alive until the
+                          call's work on the stream is done. */
 } flex_score_desc;
 
 /* ---- block mask, as consumed by flex_attn_fwd ----

@@ -26,7 +26,9 @@
  *  - Scores.  s = scale * <q_i, k_j> from the exact input values widened to
  *    fp64, then the score modification is applied to the scaled score.  The
  *    identity modification leaves it alone; the relative-position bias
- *    subtracts slope_h * (i - j), slope_h = 2^(-bias_max * (h + 1) / H).
+ *    subtracts slope_h * (i - j), slope_h = 2^(-bias_max * (h + 1) / H), or
+ *    slope_h = slopes[h] when the caller passes a per-head table (a
+ *    score_mod closing over a tensor, the op's score_mod_other_buffers).
  *
  *  - Softmax.  The online-softmax recurrence of forward_block_mn (the
  *    common.py.jinja hunk: running max, alpha rescale of the accumulator and
@@ -176,13 +178,15 @@ int oracle_block_mask(int kind, int64_t window, int64_t window_min,
  * row_max[r] = the largest visible score of the row (after the score
  * modification; -inf when the row sees no key), the third output of the
  * flex_attention op in the subtiling page's test hunks (OUTPUT_MAX).
+ * slopes: NULL, or [H] per-head slopes replacing the formula (REL_BIAS).
  * Returns 0, or -1 on a bad argument or allocation failure.
  */
 int oracle_attention_rows(const float* q, const float* k, const float* v,
                           int64_t B, int64_t H, int64_t q_len, int64_t kv_len,
                           int64_t d, int64_t dv, int mask_kind, int64_t window,
                           int64_t window_min, int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc, int score_kind,
-                          double bias_max, double scale, const int64_t* rows,
+                          double bias_max, const double* slopes, double scale,
+                          const int64_t* rows,
                           int64_t n_rows, double* out, double* lse, double* row_max) {
   if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
     return -1;
@@ -208,7 +212,7 @@ int oracle_attention_rows(const float* q, const float* k, const float* v,
     const float* qi = q + id * d;
     const float* kb = k + bh * kv_len * d;
     const float* vb = v + bh * kv_len * dv;
-    double slope = pow(2.0, -bias_max * (double)(h + 1) / (double)H);
+    double slope = slopes ? slopes[h] : pow(2.0, -bias_max * (double)(h + 1) / (double)H);
 
     /* scores for every key; masked ones are -inf */
     double mx = -INFINITY;
@@ -306,8 +310,8 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
                               int64_t H, int64_t q_len, int64_t kv_len,
                               int64_t d, int64_t dv, int mask_kind,
                               int64_t window, int64_t window_min, int64_t prefix, const int32_t* q_doc, const int32_t* kv_doc,
-                              int score_kind, double bias_max, double scale,
-                              const int64_t* heads, int64_t n_heads, double* dq,
+                              int score_kind, double bias_max, const double* slopes,
+                              double scale, const int64_t* heads, int64_t n_heads, double* dq,
                               double* dk, double* dvg) {
   if (B < 0 || H <= 0 || q_len < 0 || kv_len < 0 || d <= 0 || dv <= 0)
     return -1;
@@ -331,7 +335,7 @@ int oracle_attention_backward(const float* q, const float* k, const float* v,
       return -1;
     }
     int64_t h = bh % H;
-    double slope = pow(2.0, -bias_max * (double)(h + 1) / (double)H);
+    double slope = slopes ? slopes[h] : pow(2.0, -bias_max * (double)(h + 1) / (double)H);
     const float* qh = q + bh * q_len * d;
     const float* kh = k + bh * kv_len * d;
     const float* vh = v + bh * kv_len * dv;

@@ -72,18 +72,32 @@ def _load():
         lib.oracle_block_mask.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = (
             [f32p, f32p, f32p] + [i64] * 6 + m
-            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
+            + [ctypes.c_int, ctypes.c_double, f64p, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
         )
         lib.oracle_attention_rows.restype = ctypes.c_int
         lib.oracle_block_mask_t.argtypes = m + [i64] * 4 + [i32p] * 4
         lib.oracle_block_mask_t.restype = ctypes.c_int
         lib.oracle_attention_backward.argtypes = (
             [f32p, f32p, f32p, f32p, f32p] + [i64] * 6 + m
-            + [ctypes.c_int, ctypes.c_double, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
+            + [ctypes.c_int, ctypes.c_double, f64p, ctypes.c_double, i64p, i64, f64p, f64p, f64p]
         )
         lib.oracle_attention_backward.restype = ctypes.c_int
         _lib = lib
         return lib
+
+
+def _slopes(score: dict, H: int):
+    """A per-head slope table (score["slopes"], H values, taken exactly as
+    float64) or None for the formula."""
+    t = score.get("slopes")
+    if t is None:
+        return None
+    if hasattr(t, "detach"):
+        t = t.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(t, dtype=np.float64).reshape(-1))
+    if a.shape != (H,):
+        raise ValueError("slopes must hold one value per head")
+    return a
 
 
 def _doc_ptr(ids):
@@ -200,6 +214,8 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
     mx = np.zeros(n, np.float64) if with_max else None
     score_kind = SCORE_KINDS[score.get("kind", "identity")]
     bias_max = float(score.get("bias_max", 8.0))
+    slopes = _slopes(score, H)
+    slp = slopes.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if slopes is not None else None
     lib = _load()
     margs = _mask_args(mask, Lq, Lkv)
     f32p = ctypes.POINTER(ctypes.c_float)
@@ -209,7 +225,7 @@ def attention_rows(q, k, v, mask: dict, score: dict, scale: float, rows=None,
         if hi <= lo:
             return 0
         return lib.oracle_attention_rows(
-            qp, kp, vp, B, H, Lq, Lkv, D, Dv, *margs, score_kind, bias_max,
+            qp, kp, vp, B, H, Lq, Lkv, D, Dv, *margs, score_kind, bias_max, slp,
             float(scale),
             rows[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), hi - lo,
             out[lo:hi].ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
@@ -255,10 +271,12 @@ def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dls
     dv = np.zeros((B, H, Lkv, Dv), np.float64)
     score_kind = SCORE_KINDS[score.get("kind", "identity")]
     bias_max = float(score.get("bias_max", 8.0))
+    slopes = _slopes(score, H)
     lib = _load()
     margs = _mask_args(mask, Lq, Lkv)
     f32p = ctypes.POINTER(ctypes.c_float)
     f64p = ctypes.POINTER(ctypes.c_double)
+    slp = slopes.ctypes.data_as(f64p) if slopes is not None else None
     ptr = lambda a: a.ctypes.data_as(f32p)
     dlp = ptr(dlse) if dlse is not None else None
     heads = np.arange(B * H, dtype=np.int64) if heads is None else \
@@ -269,7 +287,7 @@ def attention_backward(q, k, v, dout, mask: dict, score: dict, scale: float, dls
         hs = heads[t:t + 1]
         return lib.oracle_attention_backward(
             ptr(q), ptr(k), ptr(v), ptr(dout), dlp, B, H, Lq, Lkv, D, Dv, *margs,
-            score_kind, bias_max, float(scale),
+            score_kind, bias_max, slp, float(scale),
             hs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1,
             dq.ctypes.data_as(f64p), dk.ctypes.data_as(f64p), dv.ctypes.data_as(f64p))
 

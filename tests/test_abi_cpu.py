@@ -116,6 +116,9 @@ def test_fwd_rejects_on_host():
     assert _fwd(mask={"kind": "sliding_window", "window": 1, "window_min": 2}) == fa.FLEX_E_INVALID_ARG
     assert _fwd(score=fa.ScoreDesc(1, 4, 8.0), H=8) == fa.FLEX_E_INVALID_ARG  # num_heads != H
     assert _fwd(score=fa.ScoreDesc(5, 1, 8.0)) == fa.FLEX_E_UNSUPPORTED
+    assert _fwd(score=fa.ScoreDesc(1, 1, 8.0, 0x1002)) == fa.FLEX_E_INVALID_ARG  # slopes misaligned
+    assert _fwd(score=fa.ScoreDesc(1, 1, float("nan"))) == fa.FLEX_E_INVALID_ARG  # no table: finite
+    assert _fwd(score=fa.ScoreDesc(1, 4, 8.0, 0x1000), H=8) == fa.FLEX_E_INVALID_ARG
     assert _fwd(ptr=0x1008) == fa.FLEX_E_INVALID_ARG            # not 16-byte aligned
     assert _fwd(ptr=None) == fa.FLEX_E_INVALID_ARG
     assert _fwd(mask={"kind": "document"}) == fa.FLEX_E_INVALID_ARG  # no row bounds
@@ -160,6 +163,7 @@ def test_bwd_rejects_on_host():
     assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(mask={"kind": "prefix_causal", "prefix": -1}) == fa.FLEX_E_INVALID_ARG
     assert _bwd(score=fa.ScoreDesc(1, 4, 8.0), H=8) == fa.FLEX_E_INVALID_ARG
+    assert _bwd(score=fa.ScoreDesc(1, 1, 8.0, 0x1001)) == fa.FLEX_E_INVALID_ARG  # slopes misaligned
     assert _bwd(ptr=0x1008) == fa.FLEX_E_INVALID_ARG           # not 16-byte aligned
     assert _bwd(ws=None) == fa.FLEX_E_INVALID_ARG              # workspace required
     assert _bwd(lse=None) == fa.FLEX_E_INVALID_ARG             # lse required

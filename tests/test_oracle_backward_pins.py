@@ -35,8 +35,9 @@ def _rand(shape, seed, scale=1.0):
 
 
 @pytest.mark.parametrize("mask", MASKS, ids=[m["kind"] for m in MASKS])
-@pytest.mark.parametrize("score", [{"kind": "identity"}, {"kind": "rel_bias", "bias_max": 8.0}],
-                         ids=["identity", "rel_bias"])
+@pytest.mark.parametrize("score", [{"kind": "identity"}, {"kind": "rel_bias", "bias_max": 8.0},
+                                   {"kind": "rel_bias", "slopes": np.array([0.9, -0.4], np.float32)}],
+                         ids=["identity", "rel_bias", "slope_table"])
 def test_backward_matches_finite_differences(mask, score):
     B, H, Lq, Lk, D, Dv = 1, 2, 9, 11, 4, 3
     q, k, v = _rand((B, H, Lq, D), 1), _rand((B, H, Lk, D), 2), _rand((B, H, Lk, Dv), 3)
@@ -83,7 +84,8 @@ def _loss64(q, k, v, dout, dlse, mask, score, scale):
         for h in range(H):
             s = scale * (q[b, h].astype(np.float64) @ k[b, h].astype(np.float64).T)
             if score.get("kind") == "rel_bias":
-                slope = 2.0 ** (-score["bias_max"] * (h + 1) / H)
+                slope = float(score["slopes"][h]) if "slopes" in score else \
+                    2.0 ** (-score["bias_max"] * (h + 1) / H)
                 s = s - slope * (i - j)
             s = np.where(m, s, -np.inf)
             for r in range(Lq):

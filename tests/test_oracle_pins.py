@@ -156,6 +156,44 @@ def test_rel_bias_geometric_series(H):
             assert abs(out[h, i] - (i - T / S)) < 1e-10
 
 
+@pytest.mark.parametrize("slopes", [[0.7, -0.3, 0.05], [1.5, 0.0, 2.0 ** -9]])
+def test_slope_table_geometric_series(slopes):
+    """A per-head slope table (a score_mod closing over a tensor): the same
+    closed forms with r = exp(-slopes[h]), for any sign; a zero slope is
+    the plain mean of the visible j."""
+    H, L, D = len(slopes), 40, 4
+    q = np.zeros((1, H, L, D), np.float32)
+    k = _rand((1, H, L, D), 13)
+    v = np.repeat(np.arange(L, dtype=np.float32)[None, None, :, None], H, axis=1)
+    table = np.array(slopes, np.float32)
+    out, lse = oracle.attention_rows(q, k, v, {"kind": "causal"},
+                                     {"kind": "rel_bias", "slopes": table}, 1.0)
+    out, lse = out.reshape(H, L), lse.reshape(H, L)
+    for h in range(H):
+        sl = float(table[h])
+        for i in range(L):
+            n = i
+            if sl == 0.0:
+                assert abs(lse[h, i] - math.log(n + 1)) < 1e-12
+                assert abs(out[h, i] - i / 2.0) < 1e-10
+                continue
+            r = math.exp(-sl)
+            S = (1 - r ** (n + 1)) / (1 - r)
+            T = r * (1 - (n + 1) * r ** n + n * r ** (n + 1)) / (1 - r) ** 2
+            assert abs(lse[h, i] - math.log(S)) < 1e-10 * max(1.0, abs(math.log(S)))
+            assert abs(out[h, i] - (i - T / S)) < 1e-8
+
+
+def test_slope_table_of_zeros_is_the_identity_score():
+    B, H, L, D = 1, 3, 70, 8
+    q, k, v = _rand((B, H, L, D), 14), _rand((B, H, L, D), 15), _rand((B, H, L, D), 16)
+    a = oracle.attention_rows(q, k, v, {"kind": "causal"}, {"kind": "identity"}, 0.3)
+    b = oracle.attention_rows(q, k, v, {"kind": "causal"},
+                              {"kind": "rel_bias", "slopes": np.zeros(H, np.float32)}, 0.3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_rel_bias_slopes_are_powers_of_two_for_8_heads():
     # with 8 heads slope_h = 2^-(h+1): a single-key row returns s_ii exactly and
     # a two-key row (j = i-1, i) has lse = log(e^{s_i,i-1 - slope} + e^{s_ii})
