@@ -202,9 +202,11 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildPar
   hi_min = block_min(hi_min, scratch);
   const bool rows_in_range = r0 + p.q_block <= p.q_len;
 
-  // pass 0 counts, pass 1 writes
+  // pass 0 counts, pass 1 writes; a row of at most kChunk kv-blocks is one
+  // chunk, whose totals are known in the same pass that places it
+  const bool one_chunk = nk <= kChunk;
   int n_part = 0, n_full = 0;
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = one_chunk ? 1 : 0; pass < 2; ++pass) {
     int seen_part = 0, seen_full = 0;
     for (int k0 = 0; k0 < nk; k0 += kChunk) {
       mark_touched(p, r0, r1, k0, touched);
@@ -220,6 +222,10 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_kernel(MaskBuildPar
       int tp, tf;
       const int bp = seen_part + block_prefix(c == 1, scratch, &tp);
       const int bf = seen_full + block_prefix(c == 2, scratch, &tf);
+      if (one_chunk) {
+        n_part = tp;
+        n_full = tf;
+      }
       if (pass == 1 && kb < nk) {
         // selected: after the selected ones before it; otherwise after all
         // selected ones and the unselected ones before it
