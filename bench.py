@@ -315,7 +315,7 @@ def write_traffic_file(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     write = 1024.0 * _counter_mean_kib(write_csv, "fwd_kernel", "WRITE_SIZE") * w_scale
     lines = [
         "# HBM traffic of the forward kernel, workload %s" % workload_name,
-        "# from: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --cold-reps 0",
+        "# from: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --cold-reps 0 --no-extra",
         "#   and the same counters over: python bench.py --copy-calibration (a 1 GiB device copy)",
         "# counter scale factors from the copy: FETCH_SIZE x%.4f, WRITE_SIZE x%.4f" % (f_scale, w_scale),
         "workload = %s" % workload_name,
