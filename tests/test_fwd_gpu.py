@@ -183,12 +183,11 @@ def test_full_tiles_demoted_to_partial_are_bitwise_equal(name, over):
 def test_empty_tiles_listed_as_partial(name, over):
     """Every empty tile listed as partial too: each is visited and, block by
     block, skipped, so the result is the same softmax.  It is not always
-    the same bits: with two q-blocks per work-group the tiles are walked in
-    descending key order, listed empty tiles can come first, and then a
-    row's first keys come through the fast path's fallback rather than the
-    exact first step, so the offset its later probabilities are rounded to
-    bf16 against can differ (out within the bf16 rounding of p, lse within
-    fp32 rounding).  Both results meet the oracle bars."""
+    the same bits: listed empty tiles can come first in the walk, and then
+    a row's first keys come through the fast path's fallback rather than
+    the exact first step, so the offset its later probabilities are rounded
+    to bf16 against can differ (out within the bf16 rounding of p, lse
+    within fp32 rounding).  Both results meet the oracle bars."""
     cfg = workload(name, **over)
     q, k, v = make_inputs(cfg)
     o0, l0, bm = run_gpu(cfg, q, k, v, out_dtype=torch.float32, lse=True)
