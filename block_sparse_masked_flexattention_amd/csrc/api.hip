@@ -385,8 +385,8 @@ int32_t flex_attn_bwd(const void* q, const void* k, const void* v, const void* o
   p.bias_max = bias_max;
   p.slopes = slopes;
   p.grad_bf16 = grad_dtype == FLEX_DTYPE_BF16 ? 1 : 0;
-  return launch_bwd(p, head_dim, v_head_dim, bm->q_block, bm->kv_block, bm->mask.kind,
-                    score_kind, static_cast<hipStream_t>(stream)) == hipSuccess
+  return launch_bwd(p, in_dtype, head_dim, v_head_dim, bm->q_block, bm->kv_block,
+                    bm->mask.kind, score_kind, static_cast<hipStream_t>(stream)) == hipSuccess
              ? FLEX_OK
              : FLEX_E_HIP;
 }

@@ -117,8 +117,9 @@ constexpr int kFwdSubtile = 1;
 constexpr int kFwdExactMax = 2;
 bool fwd_supported(int in_dtype, int head_dim, int v_head_dim, int q_block, int kv_block);
 bool bwd_supported(int in_dtype, int head_dim, int v_head_dim, int q_block, int kv_block);
-hipError_t launch_bwd(const BwdParams& p, int head_dim, int v_head_dim, int q_block,
-                      int kv_block, int mask_kind, int score_kind, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int in_dtype, int head_dim, int v_head_dim,
+                      int q_block, int kv_block, int mask_kind, int score_kind,
+                      hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int head_dim, int v_head_dim,
                       int q_block, int kv_block, int mask_kind, int score_kind,
                       int variant, hipStream_t stream);

@@ -158,7 +158,8 @@ def test_bwd_rejects_on_host():
     assert _bwd(D=96) == fa.FLEX_E_UNSUPPORTED                 # head dims 64 and 128 only
     assert _bwd(Dv=96) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(Dv=0) == fa.FLEX_E_INVALID_ARG
-    assert _bwd(dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # bf16 inputs only
+    assert _bwd(dtype=fa.DTYPE_FP32, Dv=128) == fa.FLEX_E_UNSUPPORTED  # fp32: equal head dims
+    assert _bwd(dtype=fa.DTYPE_FP32, qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(mask={"kind": "prefix_causal", "prefix": -1}) == fa.FLEX_E_INVALID_ARG
