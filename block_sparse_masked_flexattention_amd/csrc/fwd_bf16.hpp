@@ -310,41 +310,48 @@ struct Bf16Fwd {
     // instruction straight into LDS.  The instruction's LDS slot for lane i
     // is fixed (base + 16 i), so the swizzle is applied on the global side:
     // slot s = (row r, position q) receives K row swap23(r), chunk
-    // q ^ kswz(r) and V row r, chunk q ^ vswz(r) / 2.  Rows past the end of
-    // the keys are clamped to the last key; the mask gives them zero weight.
+    // q ^ kswz(r) and V row r, chunk q ^ vswz(r) / 2.  The loads go through
+    // buffer resources based at the step's first key whose size is the rows
+    // that exist, so the per-lane offsets are the same for every step (set
+    // once here) and rows past the end of the keys read as zero, with no
+    // per-step clamp; the mask gives those keys zero weight.
+    unsigned ko[NDMA], vo[NDMAV];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int sl = (wave * NDMA + j) * 64 + lane;
+      const int r = sl / CPR, q = sl % CPR;
+      ko[j] = (unsigned)((((r & ~31) | swap23(r & 31))) * ROWB) + ((unsigned)(q ^ kswz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NDMAV; ++j) {
+      const int sl = (wave * NDMAV + j) * 64 + lane;
+      const int r = sl / CPRV, q = sl % CPRV;
+      vo[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz(r) >> 1)) << 4);
+    }
     auto dma = [&](lds_t* dst, int m) {
       const int kb = tile_kb(m / SPT);
-      // a step may start past the last key (second half of a short ragged
-      // tile): then every row reads the last key
-      const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
-      const int rows_left = min(KS, p.kv_len - kv0);  // >= 1
-      const char* kt = kg + (size_t)kv0 * ROWB;
-      const char* vt = vg + (size_t)kv0 * ROWBV;
+      // the second step of a short ragged tile may start past the last key:
+      // then no row exists and every row reads as zero
+      const int kv0 = kb * KB + (m % SPT) * KS;
+      // (uniform; readfirstlane keeps the resource words in scalar
+      // registers)
+      const int rows = __builtin_amdgcn_readfirstlane(max(min(KS, p.kv_len - kv0), 0));
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(kg + (size_t)kv0 * ROWB), 0, rows * ROWB, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(vg + (size_t)kv0 * ROWBV), 0, rows * ROWBV, kBufferRsrcWord3);
       // (K and V loads alternate while both have one left: the same order
       // as one loop over both when the row widths match)
 #pragma unroll
       for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
-        if (j < NDMA) {
-          const int sl = (wave * NDMA + j) * 64 + lane;
-          const int r = sl / CPR, q = sl % CPR;
-          const int rk = min((r & ~31) | swap23(r & 31), rows_left - 1);
-          // 32-bit unsigned offsets from a uniform base: the SGPR-base form
-          const unsigned ko = (unsigned)(rk * ROWB) + ((unsigned)(q ^ kswz(r)) << 4);
-          __builtin_amdgcn_global_load_lds(kt + ko,
-                                           (__attribute__((address_space(3))) void*)(
-                                               dst + (wave * NDMA + j) * 1024),
-                                           16, 0, 0);
-        }
-        if (j < NDMAV) {
-          const int sl = (wave * NDMAV + j) * 64 + lane;
-          const int r = sl / CPRV, q = sl % CPRV;
-          const int rv = min(r, rows_left - 1);
-          const unsigned vo = (unsigned)(rv * ROWBV) + ((unsigned)(q ^ (vswz(r) >> 1)) << 4);
-          __builtin_amdgcn_global_load_lds(vt + vo,
-                                           (__attribute__((address_space(3))) void*)(
-                                               dst + STAGE + (wave * NDMAV + j) * 1024),
-                                           16, 0, 0);
-        }
+        if (j < NDMA)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              kr, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16,
+              (int)ko[j], 0, 0, 0);
+        if (j < NDMAV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vr, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMAV + j) * 1024),
+              16, (int)vo[j], 0, 0, 0);
       }
     };
 

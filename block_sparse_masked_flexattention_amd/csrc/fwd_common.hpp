@@ -16,6 +16,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kLdsBytes = 160 * 1024;
+// Word 3 of a raw buffer resource on gfx9-family parts (no swizzle, no
+// per-lane index, dword data): reads past the size return zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // value of lane l ^ 32
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32); }
