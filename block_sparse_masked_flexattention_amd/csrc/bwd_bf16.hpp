@@ -278,29 +278,46 @@ struct Bf16BwdDq {
       return min(max(v, 0), nk - 1);
     };
 
-    // K and V of step m into a stage buffer, both in V layout
+    // K and V of step m into a stage buffer, both in V layout, through
+    // buffer resources based at the step's first key whose size is the rows
+    // that exist: the per-lane offsets do not depend on the step, and rows
+    // past the end of the keys read as zero (partial tiles mask them).
+    // (The offsets are rebuilt per step from the lane index, behind an
+    // empty asm statement so that they are not hoisted: kept in registers
+    // across the loop they push the head-dim-64 instance into spills.)
     auto dma = [&](lds_t* dst, int m) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      unsigned ko[NDMA], vo[NDMAV];
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) {
+        const int sl = (wave * NDMA + j) * 64 + ln;
+        const int r = sl / CPR, q = sl % CPR;
+        ko[j] = (unsigned)(r * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+      }
+#pragma unroll
+      for (int j = 0; j < NDMAV; ++j) {
+        const int sl = (wave * NDMAV + j) * 64 + ln;
+        const int r = sl / CPRV, q = sl % CPRV;
+        vo[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
+      }
       const int kb = tile_kb(m / SPT);
-      const int kv0 = min(kb * KB + (m % SPT) * KS, p.kv_len - 1);
-      const int rows_left = min(KS, p.kv_len - kv0);
-      const char* kt = kg + (size_t)kv0 * ROWB;
-      const char* vt = vg + (size_t)kv0 * ROWBV;
+      const int kv0 = kb * KB + (m % SPT) * KS;
+      const int rows = __builtin_amdgcn_readfirstlane(max(min(KS, p.kv_len - kv0), 0));
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(kg + (size_t)kv0 * ROWB), 0, rows * ROWB, fwd::kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(vg + (size_t)kv0 * ROWBV), 0, rows * ROWBV, fwd::kBufferRsrcWord3);
 #pragma unroll
       for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
-        if (j < NDMA) {
-          const int sl = (wave * NDMA + j) * 64 + lane;
-          const int r = sl / CPR, q = sl % CPR;
-          const int rr = min(r, rows_left - 1);
-          const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
-          __builtin_amdgcn_global_load_lds(kt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
-        }
-        if (j < NDMAV) {
-          const int sl = (wave * NDMAV + j) * 64 + lane;
-          const int r = sl / CPRV, q = sl % CPRV;
-          const int rr = min(r, rows_left - 1);
-          const unsigned off = (unsigned)(rr * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
-          __builtin_amdgcn_global_load_lds(vt + off, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMAV + j) * 1024), 16, 0, 0);
-        }
+        if (j < NDMA)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              kr, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16,
+              (int)ko[j], 0, 0, 0);
+        if (j < NDMAV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              vr, (__attribute__((address_space(3))) void*)(dst + STAGE + (wave * NDMAV + j) * 1024),
+              16, (int)vo[j], 0, 0, 0);
       }
     };
 
@@ -549,31 +566,44 @@ struct Bf16BwdDkv {
       return min(max(v, 0), nq - 1);
     };
 
-    // q and dout rows of step m (32 query rows, clamped to the last row) in
-    // V layout, then -delta and a of those rows (wave 0, one dword per lane)
+    // q and dout rows of step m (32 query rows) in V layout, through buffer
+    // resources as in the dq kernel (rows past the end of the queries read
+    // as zero), then -delta and a of those rows (wave 0, one dword per lane,
+    // clamped to the last row)
+    unsigned qo[NDMA], dov[NDMAV];
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int sl = (wave * NDMA + j) * 64 + lane;
+      const int r = sl / CPR, q = sl % CPR;
+      qo[j] = (unsigned)(r * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NDMAV; ++j) {
+      const int sl = (wave * NDMAV + j) * 64 + lane;
+      const int r = sl / CPRV, q = sl % CPRV;
+      dov[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
+    }
     auto dma = [&](lds_t* dst, int m) {
       const int qbm = tile_qb(m / SPQ);
-      const int r00 = min(qbm * QB + (m % SPQ) * QS, p.q_len - 1);
-      const int rows_left = min(QS, p.q_len - r00);
-      const char* qt = qg + (size_t)r00 * ROWB;
-      const char* dt = dog + (size_t)r00 * ROWBV;
+      const int q0m = qbm * QB + (m % SPQ) * QS;
+      const int rows_in = __builtin_amdgcn_readfirstlane(max(min(QS, p.q_len - q0m), 0));
+      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(qg + (size_t)q0m * ROWB), 0, rows_in * ROWB, fwd::kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(dog + (size_t)q0m * ROWBV), 0, rows_in * ROWBV, fwd::kBufferRsrcWord3);
 #pragma unroll
       for (int j = 0; j < (NDMA > NDMAV ? NDMA : NDMAV); ++j) {
-        if (j < NDMA) {
-          const int sl = (wave * NDMA + j) * 64 + lane;
-          const int r = sl / CPR, q = sl % CPR;
-          const int rr = min(r, rows_left - 1);
-          const unsigned off = (unsigned)(rr * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
-          __builtin_amdgcn_global_load_lds(qt + off, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16, 0, 0);
-        }
-        if (j < NDMAV) {
-          const int sl = (wave * NDMAV + j) * 64 + lane;
-          const int r = sl / CPRV, q = sl % CPRV;
-          const int rr = min(r, rows_left - 1);
-          const unsigned off = (unsigned)(rr * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
-          __builtin_amdgcn_global_load_lds(dt + off, (__attribute__((address_space(3))) void*)(dst + TILE + (wave * NDMAV + j) * 1024), 16, 0, 0);
-        }
+        if (j < NDMA)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              qr, (__attribute__((address_space(3))) void*)(dst + (wave * NDMA + j) * 1024), 16,
+              (int)qo[j], 0, 0, 0);
+        if (j < NDMAV)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              dr, (__attribute__((address_space(3))) void*)(dst + TILE + (wave * NDMAV + j) * 1024),
+              16, (int)dov[j], 0, 0, 0);
       }
+      const int r00 = min(q0m, p.q_len - 1);
+      const int rows_left = min(QS, p.q_len - r00);
       if (wave == 0) {
         const int r = min(lq, rows_left - 1);
         const float* src = p.ws + (g == 0 ? 0 : rows) + (long long)head_q + r00 + r;
