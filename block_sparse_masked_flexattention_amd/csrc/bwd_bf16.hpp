@@ -28,9 +28,10 @@
 //    rows.  The S and dP accumulators start at a_i and -delta_i (read from
 //    LDS straight into them), so p = 2^(c1 s) and ds = p dP; then
 //    dv^T += dout^T p and dk^T += q^T ds read dout^T and q^T transposed.
-// K, V, q and dout tiles sit in LDS in the forward's V layout (rows in
-// order, 8-byte units XOR-swizzled by an even amount, so 16-byte pieces stay
-// whole for the row reads); a row read for an A operand takes row
+// K, V, q and dout tiles sit in LDS in the forward's V layout with one more
+// swizzle term (rows in order, 8-byte units XOR-swizzled by an even amount,
+// so 16-byte pieces stay whole for the row reads; see vswz); a row read for
+// an A operand takes row
 // swap23(lane) so that accumulator registers 8h..8h+7 hold eight
 // consecutive keys (queries), ready to be the next product's B operand.
 #pragma once
@@ -58,10 +59,23 @@ struct Int {
 };
 #define FLEXATTN_LDS(T, ptr) (*(__attribute__((address_space(3))) T*)(ptr))
 
-// V-layout swizzle of the forward: row r, 8-byte unit u at unit u ^ vswz(r)
+// Tile layout: row r, 8-byte unit u at unit u ^ vswz(r).  The backward reads
+// its tiles two ways: transposing reads (ds_read_b64_tr_b16, rows r0 .. r0 + 3
+// of a 4-row group at a time) and A-operand row reads (16 bytes per lane,
+// rows swap23(lane)).  Bits 0 and 1 of the row (the forward's V swizzle)
+// keep the transposing reads conflict-free; the term in bit 3 separates rows
+// r and r + 8, which the row reads of one 16-lane group fetch together (with
+// the forward's swizzle alone every such pair shared a bank).  Bank-conflict
+// model checked on the host for 32 and 64 four-byte banks: the row reads
+// drop from 48 to 16 extra cycles per 32-key block at head dim 64 (96 to 32
+// at 128) with 64 banks and to none with 32; the transposing reads stay
+// conflict-free.  The swizzle leaves bits 2, 4 and 5 alone, so the offsets
+// of a group's second transposing read (4 rows on), of the second 16 rows
+// and of the second 32-key block differ from the first by whole rows.
 template <int D>
 __device__ inline int vswz(int r) {
-  return D == 64 ? ((4 * (r & 1)) ^ (8 * ((r >> 1) & 1))) : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)));
+  return D == 64 ? ((4 * (r & 1)) ^ (8 * ((r >> 1) & 1)) ^ (2 * ((r >> 3) & 1)))
+                 : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)) ^ (2 * ((r >> 3) & 1)));
 }
 
 // Queries that see key kk, as one interval [lo, hi] (empty when lo > hi),
@@ -212,7 +226,7 @@ struct Bf16BwdDq {
     const char* kg = static_cast<const char*>(p.k) + (size_t)bh * p.kv_len * ROWB;
     const char* vg = static_cast<const char*>(p.v) + (size_t)bh * p.kv_len * ROWBV;
 
-    // A-operand row reads: row swap23(lq), 16-byte piece 2t + g in V layout
+    // A-operand row reads: row swap23(lq), 16-byte piece 2t + g
     // (K rows D wide, V rows DV wide)
     const int ra = swap23(lq);
     int kra[D / 16], vra[DV / 16];
@@ -278,7 +292,7 @@ struct Bf16BwdDq {
       return min(max(v, 0), nk - 1);
     };
 
-    // K and V of step m into a stage buffer, both in V layout, through
+    // K and V of step m into a stage buffer, both in the tile layout, through
     // buffer resources based at the step's first key whose size is the rows
     // that exist: the per-lane offsets do not depend on the step, and rows
     // past the end of the keys read as zero (partial tiles mask them).
@@ -566,7 +580,7 @@ struct Bf16BwdDkv {
       return min(max(v, 0), nq - 1);
     };
 
-    // q and dout rows of step m (32 query rows) in V layout, through buffer
+    // q and dout rows of step m (32 query rows) in the tile layout, through buffer
     // resources as in the dq kernel (rows past the end of the queries read
     // as zero), then -delta and a of those rows (wave 0, one dword per lane,
     // clamped to the last row)
