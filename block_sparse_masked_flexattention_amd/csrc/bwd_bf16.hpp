@@ -844,6 +844,8 @@ hipError_t bwd_pick_mask(const BwdParams& p, int mask, int score, hipStream_t s)
   }
 }
 
+#undef FLEXATTN_LDS
+
 }  // namespace bwd
 }  // namespace flexattn
 

@@ -18,7 +18,7 @@
 // against the row's visible interval), staging the other side's tile in LDS
 // 32 rows at a time.
 #pragma once
-#include "fwd_common.hpp"
+#include "bwd_bf16.hpp"
 
 namespace flexattn {
 namespace bwd32 {
@@ -28,30 +28,6 @@ using fwd::u32x4;
 
 typedef __attribute__((address_space(3))) char lds_t;
 #define FLEXATTN_LDS(T, ptr) (*(__attribute__((address_space(3))) T*)(ptr))
-
-// Keys visible from query row qi / queries that see key kk, one interval
-// each (empty when lo > hi), clipped to the other side's range.
-template <int MASK>
-__device__ inline void col_interval32(const BwdParams& p, int kk, int& lo, int& hi) {
-  lo = 0;
-  hi = p.q_len - 1;
-  if (kk >= p.kv_len) {
-    lo = 1;
-    hi = 0;
-    return;
-  }
-  if constexpr (MASK == FLEX_MASK_CAUSAL) {
-    lo = kk;
-  } else if constexpr (MASK == FLEX_MASK_SLIDING_WINDOW) {
-    lo = (int)max(0LL, (long long)kk + p.window_min);
-    hi = (int)min((long long)hi, (long long)kk + p.window);
-  } else if constexpr (MASK == FLEX_MASK_PREFIX_CAUSAL) {
-    lo = kk <= p.prefix ? 0 : kk;
-  } else if constexpr (MASK == FLEX_MASK_DOCUMENT) {
-    lo = p.col_bounds[2 * (size_t)kk];
-    hi = p.col_bounds[2 * (size_t)kk + 1];
-  }
-}
 
 // sum over the four lanes of a row (lanes 4r .. 4r + 3)
 __device__ inline float sum4(float x) {
@@ -239,7 +215,7 @@ struct Fp32BwdDkv {
       dv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     int qlo, qhi;
-    col_interval32<MASK>(p, kk, qlo, qhi);
+    bwd::col_interval<MASK>(p, kk, qlo, qhi);
     const bool live = key_ok && qlo <= qhi;
     float slope = 0.f;
     if constexpr (SCORE == FLEX_SCORE_REL_BIAS) slope = fwd::head_slope(p, h);
