@@ -300,19 +300,19 @@ struct Bf16BwdDq {
     // empty asm statement so that they are not hoisted: kept in registers
     // across the loop they push the head-dim-64 instance into spills.)
     auto dma = [&](lds_t* dst, int m) {
-      int ln = lane;
+      unsigned ln = (unsigned)lane;
       asm volatile("" : "+v"(ln));
       unsigned ko[NDMA], vo[NDMAV];
 #pragma unroll
       for (int j = 0; j < NDMA; ++j) {
-        const int sl = (wave * NDMA + j) * 64 + ln;
-        const int r = sl / CPR, q = sl % CPR;
+        const unsigned sl = (unsigned)((wave * NDMA + j) * 64) + ln;
+        const int r = (int)(sl / CPR), q = (int)(sl % CPR);
         ko[j] = (unsigned)(r * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
       }
 #pragma unroll
       for (int j = 0; j < NDMAV; ++j) {
-        const int sl = (wave * NDMAV + j) * 64 + ln;
-        const int r = sl / CPRV, q = sl % CPRV;
+        const unsigned sl = (unsigned)((wave * NDMAV + j) * 64) + ln;
+        const int r = (int)(sl / CPRV), q = (int)(sl % CPRV);
         vo[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
       }
       const int kb = tile_kb(m / SPT);
