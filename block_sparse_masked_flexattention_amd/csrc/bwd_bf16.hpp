@@ -78,6 +78,18 @@ __device__ inline int vswz(int r) {
                  : ((8 * (r & 1)) ^ (20 * ((r >> 1) & 1)) ^ (2 * ((r >> 3) & 1)));
 }
 
+// The dk/dv kernel's q and dout tiles when both are 64 wide (FULL): a
+// swizzle with a row-bit-2 term as well, conflict-free in the same model for
+// both read patterns (32 or 64 banks).  The second transposing read of a
+// 4-row group (rows r0 + 4 ..) then differs from the first in bit 2 only,
+// which moves the 8-byte unit by 2: its offset is the first one's with bit 4
+// flipped, plus 4 rows.  (Instances with a 128-wide tile keep vswz: their
+// registers are already short and the variant spilled more.)
+template <int D, bool FULL>
+__device__ inline int vswz_q(int r) {
+  return FULL ? (vswz<D>(r) ^ (2 * ((r >> 2) & 1)) ^ (4 * ((r >> 3) & 1))) : vswz<D>(r);
+}
+
 // Queries that see key kk, as one interval [lo, hi] (empty when lo > hi),
 // clipped to the query range: the transpose of row_interval.
 template <int MASK>
@@ -474,6 +486,7 @@ struct Bf16BwdDkv {
   static constexpr int NEV = DV / 32;       // dv accumulators
   static constexpr int ROWB = D * 2;        // bytes per q row
   static constexpr int ROWBV = DV * 2;      // bytes per dout row
+  static constexpr bool QF = D == 64 && DV == 64;  // tile swizzle: see vswz_q
   static constexpr int TILE = QS * ROWB;    // bytes of q per step (dout follows)
   static constexpr int ARR = TILE + QS * ROWBV;  // offset of the per-row arrays
   static constexpr int STAGEB = ARR + 2 * QS * 4;
@@ -542,19 +555,19 @@ struct Bf16BwdDkv {
     const int ra = swap23(lq);
     int qra[D / 16], dra[DV / 16];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) qra[t] = ra * ROWB + (((2 * t + g) ^ (vswz<D>(ra) >> 1)) << 4);
+    for (int t = 0; t < D / 16; ++t) qra[t] = ra * ROWB + (((2 * t + g) ^ (vswz_q<D, QF>(ra) >> 1)) << 4);
 #pragma unroll
     for (int t = 0; t < DV / 16; ++t)
-      dra[t] = ra * ROWBV + (((2 * t + g) ^ (vswz<DV>(ra) >> 1)) << 4);
+      dra[t] = ra * ROWBV + (((2 * t + g) ^ (vswz_q<DV, QF>(ra) >> 1)) << 4);
     int tro[NE], trov[NEV];
     {
       const int j = lane & 15, u = (lane >> 4) & 1;
       const int r0 = 8 * g + (j >> 2);
 #pragma unroll
-      for (int e = 0; e < NE; ++e) tro[e] = r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz<D>(r0)) << 3);
+      for (int e = 0; e < NE; ++e) tro[e] = r0 * ROWB + (((8 * e + 4 * u + (j & 3)) ^ vswz_q<D, QF>(r0)) << 3);
 #pragma unroll
       for (int e = 0; e < NEV; ++e)
-        trov[e] = r0 * ROWBV + (((8 * e + 4 * u + (j & 3)) ^ vswz<DV>(r0)) << 3);
+        trov[e] = r0 * ROWBV + (((8 * e + 4 * u + (j & 3)) ^ vswz_q<DV, QF>(r0)) << 3);
     }
 
     // transposed tile list of this kv-block
@@ -589,13 +602,13 @@ struct Bf16BwdDkv {
     for (int j = 0; j < NDMA; ++j) {
       const int sl = (wave * NDMA + j) * 64 + lane;
       const int r = sl / CPR, q = sl % CPR;
-      qo[j] = (unsigned)(r * ROWB) + ((unsigned)(q ^ (vswz<D>(r) >> 1)) << 4);
+      qo[j] = (unsigned)(r * ROWB) + ((unsigned)(q ^ (vswz_q<D, QF>(r) >> 1)) << 4);
     }
 #pragma unroll
     for (int j = 0; j < NDMAV; ++j) {
       const int sl = (wave * NDMAV + j) * 64 + lane;
       const int r = sl / CPRV, q = sl % CPRV;
-      dov[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz<DV>(r) >> 1)) << 4);
+      dov[j] = (unsigned)(r * ROWBV) + ((unsigned)(q ^ (vswz_q<DV, QF>(r) >> 1)) << 4);
     }
     auto dma = [&](lds_t* dst, int m) {
       const int qbm = tile_qb(m / SPQ);
@@ -677,25 +690,42 @@ struct Bf16BwdDkv {
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], __builtin_bit_cast(bf16x8, vf[t]), dp, 0, 0, 0);
       }
       // transposed fragments of dout and q for the two accumulations
+      // (the second read of each 4-row group: for 64-wide tiles the first
+      // offset with bit 4 flipped (see vswz_q), rebuilt per block behind an
+      // empty asm statement rather than kept in registers across the loop)
       bf16x8 dot[NEV][2], qt[NE][2];
 #pragma unroll
-      for (int e = 0; e < NEV; ++e)
+      for (int e = 0; e < NEV; ++e) {
+        int o2 = trov[e];
+        if constexpr (QF) {
+          o2 ^= 16;
+          asm volatile("" : "+v"(o2));
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const lds_t* dp0 = cur + TILE + trov[e] + 16 * hh * ROWBV;
+          const lds_t* dp1 = cur + TILE + o2 + (16 * hh + 4) * ROWBV;
           const i16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)dp0);
-          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(dp0 + 4 * ROWBV));
+          const i16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)dp1);
           dot[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+      }
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
+      for (int e = 0; e < NE; ++e) {
+        int o2 = tro[e];
+        if constexpr (QF) {
+          o2 ^= 16;
+          asm volatile("" : "+v"(o2));
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const lds_t* qp0 = cur + tro[e] + 16 * hh * ROWB;
+          const lds_t* qp1 = cur + o2 + (16 * hh + 4) * ROWB;
           const i16x4 q0v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)qp0);
-          const i16x4 q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(qp0 + 4 * ROWB));
+          const i16x4 q1v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)qp1);
           qt[e][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+      }
       // p = 2^(c1 s), masked on partial tiles; ds = p dP
       float pv[16], ds[16];
       const int lim_lo = qlo - q00 - 8 * g, lim_hi = qhi - q00 - 8 * g;
