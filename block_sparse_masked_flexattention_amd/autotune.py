@@ -61,8 +61,6 @@ def candidates(q: torch.Tensor, v: torch.Tensor):
     D, Dv = int(q.shape[3]), int(v.shape[3])
     if D not in (64, 128) or Dv not in (64, 128):
         return []
-    if q.dtype == torch.float32 and D != Dv:
-        return []
     return list(TILE_SHAPES)
 
 

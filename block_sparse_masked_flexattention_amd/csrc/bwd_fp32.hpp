@@ -16,7 +16,8 @@
 // sums and two lane exchanges.  Both kernels walk the block mask's tile lists
 // (empty tiles are never visited; in a visited tile every pair is checked
 // against the row's visible interval), staging the other side's tile in LDS
-// 32 rows at a time.
+// 32 rows at a time.  DV is the value head dim (V, out, dout and dv rows),
+// which may differ from D.
 #pragma once
 #include "bwd_bf16.hpp"
 
@@ -37,7 +38,8 @@ __device__ inline float sum4(float x) {
 }
 
 // Per query row: ws[row] = -delta = dlse_i - <dout_i, out_i>.  D / 4 lanes
-// per row, each reading 4 elements of out and dout.
+// per row (D: the rows' width, the value head dim), each reading 4 elements
+// of out and dout.
 template <int D>
 __global__ __launch_bounds__(256) void bwd32_pre_kernel(BwdParams p) {
   constexpr int LPR = D / 4;
@@ -90,15 +92,17 @@ __device__ inline void store_quarter(void* base, bool bf16, size_t row, int u, c
 // dq: one work-group per (batch, head, q-block), four lanes per query row,
 // walking the forward's tile list with each visited K and V tile in LDS.
 // ---------------------------------------------------------------------------
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 struct Fp32BwdDq {
   static constexpr int NT = 4 * QB;
-  static constexpr int NM = D / 16;  // 16-byte chunks a lane holds of a row
-  static constexpr int SUB = 32;     // keys staged at a time
+  static constexpr int NM = D / 16;    // 16-byte chunks a lane holds of a q / K row
+  static constexpr int NMV = DV / 16;  // ... of a dout / V row
+  static constexpr int SUB = 32;       // keys staged at a time
   static constexpr int TILE = SUB * D * 4;
+  static constexpr int TILEV = SUB * DV * 4;
 
   __device__ static void run(const BwdParams& p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem[TILE + TILEV];
     lds_t* const kt = (lds_t*)smem;
     lds_t* const vt = kt + TILE;
     const int tid = threadIdx.x;
@@ -109,18 +113,20 @@ struct Fp32BwdDq {
     const bool row_ok = qi < p.q_len;
     const size_t head_q = (size_t)bh * p.q_len, head_kv = (size_t)bh * p.kv_len;
     const float* qg = static_cast<const float*>(p.q) + head_q * D;
-    const float* dog = static_cast<const float*>(p.dout) + head_q * D;
+    const float* dog = static_cast<const float*>(p.dout) + head_q * DV;
     const float* kg = static_cast<const float*>(p.k) + head_kv * D;
-    const float* vg = static_cast<const float*>(p.v) + head_kv * D;
+    const float* vg = static_cast<const float*>(p.v) + head_kv * DV;
 
-    f32x4 qv[NM], dov[NM], acc[NM];
+    f32x4 qv[NM], dov[NMV], acc[NM];
     const int qr = min(qi, p.q_len - 1);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       qv[m] = *reinterpret_cast<const f32x4*>(qg + (size_t)qr * D + 16 * m + 4 * u);
-      dov[m] = *reinterpret_cast<const f32x4*>(dog + (size_t)qr * D + 16 * m + 4 * u);
       acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int m = 0; m < NMV; ++m)
+      dov[m] = *reinterpret_cast<const f32x4*>(dog + (size_t)qr * DV + 16 * m + 4 * u);
     int lo, hi;
     fwd::row_interval<MASK>(p, qi, lo, hi);
     const float lse = row_ok ? p.lse[head_q + qi] : -INFINITY;
@@ -140,7 +146,7 @@ struct Fp32BwdDq {
       const int n = min(SUB, nkeys - c0);
       __syncthreads();  // every lane is done with the previous keys
       stage_rows<D, NT>(kt, kg, k0 + c0, n);
-      stage_rows<D, NT>(vt, vg, k0 + c0, n);
+      stage_rows<DV, NT>(vt, vg, k0 + c0, n);
       __syncthreads();
       for (int j = 0; j < n; ++j) {
         f32x4 kq[NM];
@@ -148,12 +154,14 @@ struct Fp32BwdDq {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           kq[m] = FLEXATTN_LDS(f32x4, kt + (j * D + 16 * m + 4 * u) * 4);
-          const f32x4 vq = FLEXATTN_LDS(f32x4, vt + (j * D + 16 * m + 4 * u) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sd = fmaf(qv[m][e], kq[m][e], sd);
-            sp = fmaf(dov[m][e], vq[e], sp);
-          }
+          for (int e = 0; e < 4; ++e) sd = fmaf(qv[m][e], kq[m][e], sd);
+        }
+#pragma unroll
+        for (int m = 0; m < NMV; ++m) {
+          const f32x4 vq = FLEXATTN_LDS(f32x4, vt + (j * DV + 16 * m + 4 * u) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp = fmaf(dov[m][e], vq[e], sp);
         }
         sd = sum4(sd);
         sp = sum4(sp);
@@ -181,18 +189,20 @@ struct Fp32BwdDq {
 // walking the transposed tile list with each visited q and dout tile (and
 // its rows' lse and -delta) in LDS.
 // ---------------------------------------------------------------------------
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 struct Fp32BwdDkv {
   static constexpr int NT = 4 * KB;
   static constexpr int NM = D / 16;
+  static constexpr int NMV = DV / 16;
   static constexpr int SUB = 32;  // query rows staged at a time
   static constexpr int TILE = SUB * D * 4;
+  static constexpr int TILEV = SUB * DV * 4;
 
   __device__ static void run(const BwdParams& p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * TILE + 2 * SUB * 4];
+    __shared__ __attribute__((aligned(16))) char smem[TILE + TILEV + 2 * SUB * 4];
     lds_t* const qt = (lds_t*)smem;
     lds_t* const dt = qt + TILE;
-    lds_t* const rt = dt + TILE;  // lse, then -delta, of the tile's rows
+    lds_t* const rt = dt + TILEV;  // lse, then -delta, of the tile's rows
     const int tid = threadIdx.x;
     const int r = tid >> 2, u = tid & 3;
     const int bh = blockIdx.x / p.n_kb, kb = blockIdx.x % p.n_kb;
@@ -201,17 +211,20 @@ struct Fp32BwdDkv {
     const bool key_ok = kk < p.kv_len;
     const size_t head_q = (size_t)bh * p.q_len, head_kv = (size_t)bh * p.kv_len;
     const float* qg = static_cast<const float*>(p.q) + head_q * D;
-    const float* dog = static_cast<const float*>(p.dout) + head_q * D;
+    const float* dog = static_cast<const float*>(p.dout) + head_q * DV;
     const float* kg = static_cast<const float*>(p.k) + head_kv * D;
-    const float* vg = static_cast<const float*>(p.v) + head_kv * D;
+    const float* vg = static_cast<const float*>(p.v) + head_kv * DV;
 
-    f32x4 kv[NM], vv[NM], dk[NM], dv[NM];
+    f32x4 kv[NM], vv[NMV], dk[NM], dv[NMV];
     const int kr = min(kk, p.kv_len - 1);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       kv[m] = *reinterpret_cast<const f32x4*>(kg + (size_t)kr * D + 16 * m + 4 * u);
-      vv[m] = *reinterpret_cast<const f32x4*>(vg + (size_t)kr * D + 16 * m + 4 * u);
       dk[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int m = 0; m < NMV; ++m) {
+      vv[m] = *reinterpret_cast<const f32x4*>(vg + (size_t)kr * DV + 16 * m + 4 * u);
       dv[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     int qlo, qhi;
@@ -231,24 +244,26 @@ struct Fp32BwdDkv {
       const int n = min(SUB, nrows - c0), r0 = q0 + c0;
       __syncthreads();  // every lane is done with the previous rows
       stage_rows<D, NT>(qt, qg, r0, n);
-      stage_rows<D, NT>(dt, dog, r0, n);
+      stage_rows<DV, NT>(dt, dog, r0, n);
       for (int i = tid; i < n; i += NT) {
         FLEXATTN_LDS(float, rt + 4 * i) = p.lse[head_q + r0 + i];
         FLEXATTN_LDS(float, rt + 4 * (SUB + i)) = p.ws[head_q + r0 + i];
       }
       __syncthreads();
       for (int i = 0; i < n; ++i) {
-        f32x4 qq[NM], dd[NM];
+        f32x4 qq[NM], dd[NMV];
         float sd = 0.f, sp = 0.f;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           qq[m] = FLEXATTN_LDS(f32x4, qt + (i * D + 16 * m + 4 * u) * 4);
-          dd[m] = FLEXATTN_LDS(f32x4, dt + (i * D + 16 * m + 4 * u) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sd = fmaf(qq[m][e], kv[m][e], sd);
-            sp = fmaf(dd[m][e], vv[m][e], sp);
-          }
+          for (int e = 0; e < 4; ++e) sd = fmaf(qq[m][e], kv[m][e], sd);
+        }
+#pragma unroll
+        for (int m = 0; m < NMV; ++m) {
+          dd[m] = FLEXATTN_LDS(f32x4, dt + (i * DV + 16 * m + 4 * u) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp = fmaf(dd[m][e], vv[m][e], sp);
         }
         sd = sum4(sd);
         sp = sum4(sp);
@@ -261,10 +276,9 @@ struct Fp32BwdDkv {
         const float pr = vis ? expf(s - lse) : 0.f;
         const float ds = pr * (sp + ndelta);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          dv[m] += pr * dd[m];
-          dk[m] += ds * qq[m];
-        }
+        for (int m = 0; m < NMV; ++m) dv[m] += pr * dd[m];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) dk[m] += ds * qq[m];
       }
       }
     }
@@ -273,79 +287,79 @@ struct Fp32BwdDkv {
     if constexpr (MASK == FLEX_MASK_DOCUMENT)
       if (fwd::doc_poisoned(qlo, qhi)) fk = fv = fwd::opaque_nan();
     store_quarter<D>(p.dk, p.grad_bf16 != 0, head_kv + kk, u, dk, fk);
-    store_quarter<D>(p.dv, p.grad_bf16 != 0, head_kv + kk, u, dv, fv);
+    store_quarter<DV>(p.dv, p.grad_bf16 != 0, head_kv + kk, u, dv, fv);
   }
 };
 
 #undef FLEXATTN_LDS
 
-template <int D, int QB, int KB, int MASK, int SCORE>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, Fp32BwdDq<D, QB, KB, MASK, SCORE>::NT)))
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Fp32BwdDq<D, DV, QB, KB, MASK, SCORE>::NT)))
 void bwd32_dq_kernel(BwdParams p) {
-  Fp32BwdDq<D, QB, KB, MASK, SCORE>::run(p);
+  Fp32BwdDq<D, DV, QB, KB, MASK, SCORE>::run(p);
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, Fp32BwdDkv<D, QB, KB, MASK, SCORE>::NT)))
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Fp32BwdDkv<D, DV, QB, KB, MASK, SCORE>::NT)))
 void bwd32_dkv_kernel(BwdParams p) {
-  Fp32BwdDkv<D, QB, KB, MASK, SCORE>::run(p);
+  Fp32BwdDkv<D, DV, QB, KB, MASK, SCORE>::run(p);
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 hipError_t launch_bwd32_one(const BwdParams& p, hipStream_t s) {
   const long long rows = (long long)p.B * p.H * p.q_len;
   if (rows > 0) {
-    const long long threads = rows * (D / 4);
-    hipLaunchKernelGGL(bwd32_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+    const long long threads = rows * (DV / 4);
+    hipLaunchKernelGGL(bwd32_pre_kernel<DV>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // dq == nullptr: WRITE_DQ off, the dq kernel is skipped
   const long long nq = p.dq != nullptr ? (long long)p.B * p.H * p.n_qb : 0;
   if (nq > 0) {
-    hipLaunchKernelGGL((bwd32_dq_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
-                       dim3(Fp32BwdDq<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd32_dq_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nq),
+                       dim3(Fp32BwdDq<D, DV, QB, KB, MASK, SCORE>::NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const long long nkv = (long long)p.B * p.H * p.n_kb;
   if (nkv > 0) {
-    hipLaunchKernelGGL((bwd32_dkv_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nkv),
-                       dim3(Fp32BwdDkv<D, QB, KB, MASK, SCORE>::NT), 0, s, p);
+    hipLaunchKernelGGL((bwd32_dkv_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nkv),
+                       dim3(Fp32BwdDkv<D, DV, QB, KB, MASK, SCORE>::NT), 0, s, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-template <int D, int QB, int KB, int MASK>
+template <int D, int DV, int QB, int KB, int MASK>
 hipError_t bwd32_pick_score(const BwdParams& p, int score, hipStream_t s) {
-  if (score == FLEX_SCORE_REL_BIAS) return launch_bwd32_one<D, QB, KB, MASK, FLEX_SCORE_REL_BIAS>(p, s);
-  return launch_bwd32_one<D, QB, KB, MASK, FLEX_SCORE_IDENTITY>(p, s);
+  if (score == FLEX_SCORE_REL_BIAS) return launch_bwd32_one<D, DV, QB, KB, MASK, FLEX_SCORE_REL_BIAS>(p, s);
+  return launch_bwd32_one<D, DV, QB, KB, MASK, FLEX_SCORE_IDENTITY>(p, s);
 }
 
-template <int D, int QB, int KB>
+template <int D, int DV, int QB, int KB>
 hipError_t bwd32_pick_mask(const BwdParams& p, int mask, int score, hipStream_t s) {
   switch (mask) {
     case FLEX_MASK_NOOP:
-      return bwd32_pick_score<D, QB, KB, FLEX_MASK_NOOP>(p, score, s);
+      return bwd32_pick_score<D, DV, QB, KB, FLEX_MASK_NOOP>(p, score, s);
     case FLEX_MASK_CAUSAL:
-      return bwd32_pick_score<D, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
+      return bwd32_pick_score<D, DV, QB, KB, FLEX_MASK_CAUSAL>(p, score, s);
     case FLEX_MASK_SLIDING_WINDOW:
-      return bwd32_pick_score<D, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
+      return bwd32_pick_score<D, DV, QB, KB, FLEX_MASK_SLIDING_WINDOW>(p, score, s);
     case FLEX_MASK_DOCUMENT:
     case FLEX_MASK_DOCUMENT_CAUSAL:
-      return bwd32_pick_score<D, QB, KB, FLEX_MASK_DOCUMENT>(p, score, s);
+      return bwd32_pick_score<D, DV, QB, KB, FLEX_MASK_DOCUMENT>(p, score, s);
     default:
-      return bwd32_pick_score<D, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
+      return bwd32_pick_score<D, DV, QB, KB, FLEX_MASK_PREFIX_CAUSAL>(p, score, s);
   }
 }
 
 }  // namespace bwd32
 }  // namespace flexattn
 
-#define FLEXATTN_BWD32_UNIT(NAME, D, QB, KB)                                  \
+#define FLEXATTN_BWD32_UNIT(NAME, D, DV, QB, KB)                              \
   namespace flexattn {                                                      \
   hipError_t NAME(const BwdParams& p, int mask, int score, hipStream_t s) { \
-    return bwd32::bwd32_pick_mask<D, QB, KB>(p, mask, score, s);            \
+    return bwd32::bwd32_pick_mask<D, DV, QB, KB>(p, mask, score, s);        \
   }                                                                         \
   }

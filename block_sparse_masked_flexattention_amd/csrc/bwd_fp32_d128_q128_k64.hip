@@ -1,4 +1,4 @@
 // fp32 inputs, head dim 128, 128x64 tiles: backward kernel instances of bwd_fp32.hpp.
 #include "bwd_fp32.hpp"
 
-FLEXATTN_BWD32_UNIT(launch_bwd_fp32_d128_q128_k64, 128, 128, 64)
+FLEXATTN_BWD32_UNIT(launch_bwd_fp32_d128_q128_k64, 128, 128, 128, 64)

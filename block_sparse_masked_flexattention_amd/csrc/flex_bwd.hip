@@ -1,7 +1,7 @@
 // flex_bwd.hip -- dispatch of the backward over its built instances (input
 // dtype, head dim, value head dim, q block, kv block); the instances live in
 // the bwd_*.hip units, the kernels in bwd_bf16.hpp (bf16 inputs, any pair of
-// head dims 64 / 128) and bwd_fp32.hpp (fp32 inputs, equal head dims).
+// head dims 64 / 128) and bwd_fp32.hpp (fp32 inputs, likewise).
 #include "internal.hpp"
 
 namespace flexattn {
@@ -26,6 +26,12 @@ hipError_t launch_bwd_fp32_d64_q128_k128(const BwdParams&, int, int, hipStream_t
 hipError_t launch_bwd_fp32_d128_q64_k64(const BwdParams&, int, int, hipStream_t);
 hipError_t launch_bwd_fp32_d128_q128_k64(const BwdParams&, int, int, hipStream_t);
 hipError_t launch_bwd_fp32_d128_q128_k128(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d64v128_q64_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d64v128_q128_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d64v128_q128_k128(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d128v64_q64_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d128v64_q128_k64(const BwdParams&, int, int, hipStream_t);
+hipError_t launch_bwd_fp32_d128v64_q128_k128(const BwdParams&, int, int, hipStream_t);
 
 namespace {
 
@@ -53,6 +59,12 @@ const BwdInstance kBwdInstances[] = {
     {FLEX_DTYPE_FP32, 128, 128, 64, 64, launch_bwd_fp32_d128_q64_k64},
     {FLEX_DTYPE_FP32, 128, 128, 128, 64, launch_bwd_fp32_d128_q128_k64},
     {FLEX_DTYPE_FP32, 128, 128, 128, 128, launch_bwd_fp32_d128_q128_k128},
+    {FLEX_DTYPE_FP32, 64, 128, 64, 64, launch_bwd_fp32_d64v128_q64_k64},
+    {FLEX_DTYPE_FP32, 64, 128, 128, 64, launch_bwd_fp32_d64v128_q128_k64},
+    {FLEX_DTYPE_FP32, 64, 128, 128, 128, launch_bwd_fp32_d64v128_q128_k128},
+    {FLEX_DTYPE_FP32, 128, 64, 64, 64, launch_bwd_fp32_d128v64_q64_k64},
+    {FLEX_DTYPE_FP32, 128, 64, 128, 64, launch_bwd_fp32_d128v64_q128_k64},
+    {FLEX_DTYPE_FP32, 128, 64, 128, 128, launch_bwd_fp32_d128v64_q128_k128},
 };
 
 BwdUnit find_bwd(int in_dtype, int head_dim, int v_head_dim, int q_block, int kv_block) {

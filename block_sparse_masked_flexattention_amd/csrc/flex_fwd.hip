@@ -26,6 +26,12 @@ FLEXATTN_DECLARE(launch_fwd_fp32_d64_q128_k128)
 FLEXATTN_DECLARE(launch_fwd_fp32_d128_q64_k64)
 FLEXATTN_DECLARE(launch_fwd_fp32_d128_q128_k64)
 FLEXATTN_DECLARE(launch_fwd_fp32_d128_q128_k128)
+FLEXATTN_DECLARE(launch_fwd_fp32_d64v128_q64_k64)
+FLEXATTN_DECLARE(launch_fwd_fp32_d64v128_q128_k64)
+FLEXATTN_DECLARE(launch_fwd_fp32_d64v128_q128_k128)
+FLEXATTN_DECLARE(launch_fwd_fp32_d128v64_q64_k64)
+FLEXATTN_DECLARE(launch_fwd_fp32_d128v64_q128_k64)
+FLEXATTN_DECLARE(launch_fwd_fp32_d128v64_q128_k128)
 #undef FLEXATTN_DECLARE
 
 namespace {
@@ -54,6 +60,12 @@ const FwdInstance kFwdInstances[] = {
     {FLEX_DTYPE_FP32, 128, 128, 64, 64, launch_fwd_fp32_d128_q64_k64},
     {FLEX_DTYPE_FP32, 128, 128, 128, 64, launch_fwd_fp32_d128_q128_k64},
     {FLEX_DTYPE_FP32, 128, 128, 128, 128, launch_fwd_fp32_d128_q128_k128},
+    {FLEX_DTYPE_FP32, 64, 128, 64, 64, launch_fwd_fp32_d64v128_q64_k64},
+    {FLEX_DTYPE_FP32, 64, 128, 128, 64, launch_fwd_fp32_d64v128_q128_k64},
+    {FLEX_DTYPE_FP32, 64, 128, 128, 128, launch_fwd_fp32_d64v128_q128_k128},
+    {FLEX_DTYPE_FP32, 128, 64, 64, 64, launch_fwd_fp32_d128v64_q64_k64},
+    {FLEX_DTYPE_FP32, 128, 64, 128, 64, launch_fwd_fp32_d128v64_q128_k64},
+    {FLEX_DTYPE_FP32, 128, 64, 128, 128, launch_fwd_fp32_d128v64_q128_k128},
 };
 
 FwdUnit find_fwd(int in_dtype, int head_dim, int v_head_dim, int q_block, int kv_block) {

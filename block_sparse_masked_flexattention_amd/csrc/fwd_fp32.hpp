@@ -7,30 +7,36 @@
 // v_mfma_f32_32x32x2_f32 and p is not rounded before P V.  The lane layout is
 // the bf16 kernel's (S^T = K Q^T, K rows with bits 2 and 3 swapped, one query
 // row per lane); V stays row-major in LDS because an fp32 operand is one
-// element per lane.  The running max is updated exactly every tile.
+// element per lane.  The running max is updated exactly every tile.  DV is
+// the value head dim (V rows, the output), which may differ from D.
 #pragma once
 #include "fwd_common.hpp"
 
 namespace flexattn {
 namespace fwd {
 
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 struct Fp32Fwd {
   static constexpr int NW = QB / 32;
   static constexpr int NT = NW * 64;
   static constexpr int NB = KB / 32;
-  static constexpr int NE = D / 32;
-  static constexpr int ROWB = D * 4;
-  static constexpr int TILE = KB * ROWB;
-  static constexpr int STAGES = (4 * TILE <= kLdsBytes) ? 2 : 1;
+  static constexpr int NE = DV / 32;
+  static constexpr int ROWB = D * 4;         // bytes per K row
+  static constexpr int ROWBV = DV * 4;       // bytes per V row
+  static constexpr int TILE = KB * ROWB;     // K tile (V follows)
+  static constexpr int TILEV = KB * ROWBV;
+  static constexpr int STAGEB = TILE + TILEV;
+  static constexpr int STAGES = (2 * STAGEB <= kLdsBytes) ? 2 : 1;
   static constexpr int CPR = ROWB / 16;
+  static constexpr int CPRV = ROWBV / 16;
   static constexpr int LPT = KB * CPR / NT;
-  static_assert(KB * CPR % NT == 0, "tile load split");
+  static constexpr int LPTV = KB * CPRV / NT;
+  static_assert(KB * CPR % NT == 0 && KB * CPRV % NT == 0, "tile load split");
 
   __device__ static inline int k_off(int m, int c) { return m * ROWB + ((c ^ (m & 7)) << 4); }
 
   __device__ static void run(const FwdParams& p) {
-    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem_raw[STAGES * STAGEB];
     typedef __attribute__((address_space(3))) char lds_t;
     lds_t* smem = (lds_t*)smem_raw;
     const int tid = threadIdx.x;
@@ -47,7 +53,7 @@ struct Fp32Fwd {
     const size_t head_kv = (size_t)bh * p.kv_len;
     const char* qg = static_cast<const char*>(p.q) + head_q * ROWB;
     const char* kg = static_cast<const char*>(p.k) + head_kv * ROWB;
-    const char* vg = static_cast<const char*>(p.v) + head_kv * ROWB;
+    const char* vg = static_cast<const char*>(p.v) + head_kv * ROWBV;
 
     // Q fragments: lane group g holds d = 8u + 4g + e4
     f32x4 qf[D / 8];
@@ -77,7 +83,7 @@ struct Fp32Fwd {
       return __builtin_amdgcn_readfirstlane(min(max(v, 0), nk - 1));
     };
 
-    u32x4 sk[LPT], sv[LPT];
+    u32x4 sk[LPT], sv[LPTV];
     auto fetch = [&](int kb) {
       const int kv0 = kb * KB;
       const bool ragged = kv0 + KB > p.kv_len;
@@ -88,18 +94,30 @@ struct Fp32Fwd {
         const size_t off = (size_t)(kv0 + row) * ROWB + col * 16;
         const bool ok = !ragged || kv0 + row < p.kv_len;
         sk[it] = ok ? ld_global16(kg + off) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int it = 0; it < LPTV; ++it) {
+        const int id = tid + it * NT;
+        const int row = id / CPRV, col = id % CPRV;
+        const size_t off = (size_t)(kv0 + row) * ROWBV + col * 16;
+        const bool ok = !ragged || kv0 + row < p.kv_len;
         sv[it] = ok ? ld_global16(vg + off) : u32x4{0, 0, 0, 0};
       }
     };
     auto stash = [&](int buf) {
-      const int base = buf * 2 * TILE;
+      const int base = buf * STAGEB;
 #pragma unroll
       for (int it = 0; it < LPT; ++it) {
         const int id = tid + it * NT;
         const int row = id / CPR, col = id % CPR;
         const int m = (row & ~31) | swap23(row & 31);
         *(__attribute__((address_space(3))) u32x4*)(smem + base + k_off(m, col)) = sk[it];
-        *(__attribute__((address_space(3))) u32x4*)(smem + base + TILE + row * ROWB + col * 16) =
+      }
+#pragma unroll
+      for (int it = 0; it < LPTV; ++it) {
+        const int id = tid + it * NT;
+        const int row = id / CPRV, col = id % CPRV;
+        *(__attribute__((address_space(3))) u32x4*)(smem + base + TILE + row * ROWBV + col * 16) =
             sv[it];
       }
     };
@@ -118,7 +136,7 @@ struct Fp32Fwd {
     __syncthreads();
 
     for (int n = 0; n < ntiles; ++n) {
-      const int base = STAGES == 2 ? (n & 1) * 2 * TILE : 0;
+      const int base = STAGES == 2 ? (n & 1) * STAGEB : 0;
       const int kv0 = kb_cur * KB;
       const bool partial = n < np || q_ragged || kv0 + KB > p.kv_len;
       const bool has_next = n + 1 < ntiles;
@@ -200,7 +218,7 @@ struct Fp32Fwd {
           for (int r = 0; r < 16; ++r) {
             const int kv = 32 * b + 16 * (r >> 3) + 8 * g + (r & 7);
             const float vv = *(__attribute__((address_space(3))) float*)(
-                smem + base + TILE + kv * ROWB + (32 * e + lq) * 4);
+                smem + base + TILE + kv * ROWBV + (32 * e + lq) * 4);
             o[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s[b][r], o[e], 0, 0, 0);
           }
 
@@ -226,7 +244,7 @@ struct Fp32Fwd {
     if constexpr (MASK == FLEX_MASK_DOCUMENT) poison = doc_poisoned(lo, hi);
     if (poison) inv = opaque_nan();
     if (qi < p.q_len) {
-      write_out_row<NE>(p, head_q + qi, D, g, o, inv);
+      write_out_row<NE>(p, head_q + qi, DV, g, o, inv);
       if (p.lse != nullptr && g == 0)
         p.lse[head_q + qi] = poison ? opaque_nan()
                                     : live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;

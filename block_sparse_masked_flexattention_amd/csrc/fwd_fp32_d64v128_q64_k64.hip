@@ -1,0 +1,5 @@
+// fp32 inputs, head dim 64, value head dim 128, 64x64 tiles: kernel instances of
+// fwd_kernel.hpp.
+#include "fwd_kernel.hpp"
+
+FLEXATTN_FWD_UNIT(launch_fwd_fp32_d64v128_q64_k64, false, 64, 128, 64, 64)

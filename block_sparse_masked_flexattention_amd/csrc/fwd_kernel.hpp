@@ -19,10 +19,10 @@ void bf16_fwd_kernel(FwdParams p) {
   Bf16Fwd<D, DV, QB, KB, MASK, SCORE, SUB, XMAX>::run(p);
 }
 
-template <int D, int QB, int KB, int MASK, int SCORE>
+template <int D, int DV, int QB, int KB, int MASK, int SCORE>
 __global__ __attribute__((amdgpu_flat_work_group_size(
-    1, Fp32Fwd<D, QB, KB, MASK, SCORE>::NT))) void fp32_fwd_kernel(FwdParams p) {
-  Fp32Fwd<D, QB, KB, MASK, SCORE>::run(p);
+    1, Fp32Fwd<D, DV, QB, KB, MASK, SCORE>::NT))) void fp32_fwd_kernel(FwdParams p) {
+  Fp32Fwd<D, DV, QB, KB, MASK, SCORE>::run(p);
 }
 
 template <bool BF16, int D, int DV, int QB, int KB, int MASK, int SCORE, bool SUB, bool XMAX>
@@ -33,9 +33,8 @@ hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bf16_fwd_kernel<D, DV, QB, KB, MASK, SCORE, SUB, XMAX>), dim3((unsigned)nwg),
                        dim3(Bf16Fwd<D, DV, QB, KB, MASK, SCORE, SUB, XMAX>::NT), 0, stream, p);
   } else {
-    static_assert(BF16 || DV == D, "fp32 inputs: value head dim = head dim");
-    hipLaunchKernelGGL((fp32_fwd_kernel<D, QB, KB, MASK, SCORE>), dim3((unsigned)nwg),
-                       dim3(Fp32Fwd<D, QB, KB, MASK, SCORE>::NT), 0, stream, p);
+    hipLaunchKernelGGL((fp32_fwd_kernel<D, DV, QB, KB, MASK, SCORE>), dim3((unsigned)nwg),
+                       dim3(Fp32Fwd<D, DV, QB, KB, MASK, SCORE>::NT), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -265,10 +265,9 @@ int32_t flex_attn_build_block_mask_t(const flex_mask_desc* mask, int32_t q_len,
  *   key), the third output of the op (OUTPUT_MAX).  Requesting it runs the
  *   exact running max on every block.
  *   opt: host pointer, NULL = defaults (every option 0).
- * Built instances: in_dtype BF16 with head_dim and v_head_dim each 64 or 128,
- * or FP32 with head_dim = v_head_dim = 64 or 128; (q_block, kv_block) in
- * {(64, 64), (128, 64), (128, 128)}; any mask kind and score kind; out_dtype
- * BF16 or FP32.  q_len, kv_len >= 0 (ragged last
+ * Built instances: in_dtype BF16 or FP32, head_dim and v_head_dim each 64 or
+ * 128; (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}; any mask
+ * kind and score kind; out_dtype BF16 or FP32.  q_len, kv_len >= 0 (ragged last
  * blocks are fine), B, H >= 0, B * H * n_q_blocks < 2^31.
  * Debugging: with the environment variable FLEXATTN_DEBUG_LDS_POISON set
  * (to anything but "0"; read on every call) the BF16-input forward fills
@@ -316,10 +315,9 @@ int32_t flex_attn_bwd_workspace_floats(int32_t B, int32_t H, int32_t q_len,
  *   its place, and dk and dv are the same as with dq requested.
  *   workspace: device fp32, flex_attn_bwd_workspace_floats() floats, owned by
  *   the caller; its contents on entry are ignored and left undefined.
- * Built instances: in_dtype BF16 with head_dim and v_head_dim each 64 or
- * 128, or in_dtype FP32 with head_dim = v_head_dim = 64 or 128; (q_block,
- * kv_block) in {(64, 64), (128, 64), (128, 128)}, any mask kind and score
- * kind.  BF16 inputs take the products on the matrix cores (p and ds rounded
+ * Built instances: in_dtype BF16 or FP32, head_dim and v_head_dim each 64 or
+ * 128; (q_block, kv_block) in {(64, 64), (128, 64), (128, 128)}, any mask
+ * kind and score kind.  BF16 inputs take the products on the matrix cores (p and ds rounded
  * to bf16, fp32 sums); FP32 inputs keep every product and sum in fp32.
  * Errors: FLEX_E_INVALID_ARG, FLEX_E_UNSUPPORTED (other instances, scale 0
  * or not finite), FLEX_E_HIP. */

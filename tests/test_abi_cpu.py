@@ -109,7 +109,7 @@ def test_fwd_rejects_on_host():
     assert _fwd(D=96) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(Dv=96) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(Dv=0) == fa.FLEX_E_INVALID_ARG
-    assert _fwd(Dv=128, dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED  # fp32: Dv = D only
+    assert _fwd(Dv=96, dtype=fa.DTYPE_FP32) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED
     assert _fwd(scale=float("nan")) == fa.FLEX_E_UNSUPPORTED
@@ -158,7 +158,7 @@ def test_bwd_rejects_on_host():
     assert _bwd(D=96) == fa.FLEX_E_UNSUPPORTED                 # head dims 64 and 128 only
     assert _bwd(Dv=96) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(Dv=0) == fa.FLEX_E_INVALID_ARG
-    assert _bwd(dtype=fa.DTYPE_FP32, Dv=128) == fa.FLEX_E_UNSUPPORTED  # fp32: equal head dims
+    assert _bwd(dtype=fa.DTYPE_FP32, Dv=96) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(dtype=fa.DTYPE_FP32, qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(qb=32, kb=32) == fa.FLEX_E_UNSUPPORTED
     assert _bwd(scale=0.0) == fa.FLEX_E_UNSUPPORTED

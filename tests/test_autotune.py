@@ -19,8 +19,9 @@ def test_candidates():
     assert at.candidates(q, v) == [(64, 64), (128, 64), (128, 128)]
     assert at.candidates(q, _t((1, 1, 8, 128))) == [(64, 64), (128, 64), (128, 128)]
     assert at.candidates(_t((1, 1, 8, 96)), v) == []
-    # fp32 inputs: equal head dims only
-    assert at.candidates(_t((1, 1, 8, 64), torch.float32), _t((1, 1, 8, 128), torch.float32)) == []
+    assert at.candidates(_t((1, 1, 8, 64), torch.float32), _t((1, 1, 8, 128), torch.float32)) == \
+        [(64, 64), (128, 64), (128, 128)]
+    assert at.candidates(_t((1, 1, 8, 128), torch.float32), _t((1, 1, 8, 96), torch.float32)) == []
 
 
 def test_signature_separates_what_matters():

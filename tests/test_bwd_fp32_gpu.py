@@ -15,7 +15,8 @@ forward's fp32 one,
     oracle but about 2^-24 |dP| per term in fp32)
 
 plus half a bf16 ulp of ref for bf16 gradients.  Cases span every mask kind,
-both head dims, every tile shape, ragged tails on both sides, the relative
+both head dims, value head dims unlike them, every tile shape, ragged tails
+on both sides, the relative
 bias (formula and per-head table), the lse gradient, a negative scale,
 WRITE_DQ off, empty ranges and unsorted document ids."""
 import numpy as np
@@ -136,6 +137,18 @@ CASES = [
                               score={"kind": "rel_bias", "bias_max": 8.0})),
     ("long_causal_d128", dict(B=1, H=1, q_len=200, kv_len=450, mask={"kind": "noop"},
                               q_block=128, kv_block=64)),
+    # value head dim unlike the key head dim, every tile shape
+    ("prefix_causal", dict(B=1, H=2, q_len=520, kv_len=520, dv=128,
+                           mask={"kind": "prefix_causal", "prefix": 200})),
+    ("sliding_window", dict(B=1, H=1, q_len=700, kv_len=700, dv=128, q_block=128, kv_block=64,
+                            mask={"kind": "sliding_window", "window": 100, "window_min": 3})),
+    ("document_causal", dict(B=1, H=2, q_len=500, kv_len=500, dv=128, q_block=128, kv_block=128,
+                             doc_len_min=1, doc_len_max=200)),
+    ("long_causal_d128", dict(B=1, H=2, q_len=333, kv_len=333, dv=64)),
+    ("long_causal_d128", dict(B=1, H=3, q_len=300, kv_len=300, dv=64, q_block=128, kv_block=64,
+                              score={"kind": "rel_bias", "bias_max": 8.0})),
+    ("long_causal_d128", dict(B=1, H=1, q_len=200, kv_len=450, dv=64, mask={"kind": "noop"},
+                              q_block=64, kv_block=64)),
 ]
 
 
@@ -144,13 +157,13 @@ def test_fp32_parity(name, over):
     _case(name, over)
 
 
-@pytest.mark.parametrize("i", [0, 4, 13])
+@pytest.mark.parametrize("i", [0, 4, 13, 19, 21])
 def test_fp32_bf16_grads(i):
     name, over = CASES[i]
     _case(name, over, grad_dtype=torch.bfloat16)
 
 
-@pytest.mark.parametrize("i", [2, 6, 11, 16])
+@pytest.mark.parametrize("i", [2, 6, 11, 16, 20, 22])
 def test_fp32_lse_gradient(i):
     name, over = CASES[i]
     _case(name, over, with_dlse=True)
@@ -167,7 +180,7 @@ def test_fp32_slope_table():
                                   score={"kind": "rel_bias", "slopes": table}))
 
 
-@pytest.mark.parametrize("i", [3, 14])
+@pytest.mark.parametrize("i", [3, 14, 23])
 def test_fp32_write_dq_off(i):
     """WRITE_DQ off: no dq, and dk / dv bit-identical to the run with dq."""
     name, over = CASES[i]

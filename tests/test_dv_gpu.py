@@ -2,7 +2,8 @@
 (the V_HEAD_DIM of the pages' kernel template, "[Inductor][Flex Attention]
 Add Subtiling Option for Alpha Scaling", flex_attention.py hunks) vs the fp64
 oracle, which takes Dv as its own argument.  Bars as for the other forward
-tests: out 1e-2 (fp32 output; bf16 output adds half a bf16 ulp), lse 1e-3."""
+tests: bf16 inputs out 1e-2 (fp32 output; bf16 output adds half a bf16 ulp),
+lse 1e-3; fp32 inputs the fp32 bar of tests/parity.py on out and lse."""
 import numpy as np
 import pytest
 import torch
@@ -80,3 +81,28 @@ def test_full_size_sampled():
     """The prefix workload's shape with a 128-wide value head, sampled rows."""
     cfg = workload("prefix_causal", dv=128)
     _run(cfg, rows=sample_rows(cfg))
+
+
+FP32_CASES = [
+    (64, 128, 64, 64, dict(mask={"kind": "prefix_causal", "prefix": 300})),
+    (64, 128, 128, 64, dict(mask={"kind": "sliding_window", "window": 200, "window_min": 3})),
+    (64, 128, 128, 128, dict(mask={"kind": "causal"}, score={"kind": "rel_bias", "bias_max": 8.0}, H=4)),
+    (128, 64, 64, 64, dict(mask={"kind": "document_causal"}, doc_len_min=20, doc_len_max=300)),
+    (128, 64, 128, 64, dict(mask={"kind": "noop"}, kv_len=650)),
+    (128, 64, 128, 128, dict(mask={"kind": "causal"}, q_len=333, kv_len=333)),
+]
+
+
+@pytest.mark.parametrize("d,dv,qb,kb,over", FP32_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-{i}" for i, c in enumerate(FP32_CASES)])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_fp32_parity(d, dv, qb, kb, over, out_dtype):
+    """fp32 inputs with a value head dim unlike the key head dim."""
+    base = dict(B=1, H=2, q_len=777, kv_len=777, d=d, dv=dv, q_block=qb, kv_block=kb,
+                score={"kind": "identity"})
+    base.update(over)
+    cfg = workload("prefix_causal", **base)
+    cfg["dtype"] = "fp32"
+    cfg["scale"] = fa.default_scale(d)
+    print("case fp32", d, dv, qb, kb, over, out_dtype, flush=True)
+    _run(cfg, out_dtype=out_dtype)
