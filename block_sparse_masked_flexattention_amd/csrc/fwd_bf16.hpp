@@ -127,6 +127,7 @@ struct Bf16Fwd {
   static_assert(KB % KS == 0 && NDMA * 64 * NW == KS * CPR, "step split");
   static_assert(NDMAV * 64 * NW == KS * CPRV, "step split (V)");
   static_assert(D == 64 || D == 128, "head dim");
+  static_assert((NW & (NW - 1)) == 0, "row-group rotation");
   static_assert((STAGE + STAGEV) % (16 * NT) == 0, "stage fill");
   static_assert(DV == 64 || DV == 128, "value head dim");
 
@@ -193,6 +194,15 @@ struct Bf16Fwd {
     int bh, qb;
     wg_to_tile(p.n_qb, bh, qb);
     const int h = bh % p.H;
+    // The wave's 32-row group of the q-block, rotated by the item: the waves
+    // of a work-group run their steps together (one barrier per step), and
+    // near the diagonal or a window edge the groups see unequal numbers of
+    // blocks per step; with wave w of every resident work-group on the same
+    // SIMD, equal groups would stack the same imbalance there.  The rotation
+    // differs between consecutive items and between items 32 apart, the
+    // neighbours on one CU under either fill order.
+    const int item = (int)(blockIdx.x >> 3);
+    const int rw = (wave + item + (item >> 5)) & (NW - 1);
     const int q0 = qb * QB;
     const bool q_ragged = q0 + QB > p.q_len;
 
@@ -273,7 +283,7 @@ struct Bf16Fwd {
     u32x4 qf[NQ][D / 16];
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-      qi[c] = q0 + (wave * NQ + c) * 32 + lq;
+      qi[c] = q0 + (rw * NQ + c) * 32 + lq;
       // rows past the end load the last row (zeroed below): no branch
       // around the loads
       const int qr = min(qi[c], p.q_len - 1);
@@ -653,8 +663,8 @@ struct Bf16Fwd {
       if (poison) inv = opaque_nan();
       if (lds_out)
         store_rows_bf16_lds<NE>(buf[0] + wave * 32 * OROW,
-                                static_cast<char*>(p.out) + (head_q + (size_t)(q0 + wave * 32)) * OROW,
-                                p.q_len - (q0 + wave * 32), o[c], inv, lane);
+                                static_cast<char*>(p.out) + (head_q + (size_t)(q0 + rw * 32)) * OROW,
+                                p.q_len - (q0 + rw * 32), o[c], inv, lane);
       if (qi[c] < p.q_len) {
         if (!lds_out) write_out_row<NE>(p, head_q + qi[c], DV, g, o[c], inv);
         if (p.lse != nullptr && g == 0)
