@@ -194,15 +194,7 @@ struct Bf16Fwd {
     int bh, qb;
     wg_to_tile(p.n_qb, bh, qb);
     const int h = bh % p.H;
-    // The wave's 32-row group of the q-block, rotated by the item: the waves
-    // of a work-group run their steps together (one barrier per step), and
-    // near the diagonal or a window edge the groups see unequal numbers of
-    // blocks per step; with wave w of every resident work-group on the same
-    // SIMD, equal groups would stack the same imbalance there.  The rotation
-    // differs between consecutive items and between items 32 apart, the
-    // neighbours on one CU under either fill order.
-    const int item = (int)(blockIdx.x >> 3);
-    const int rw = (wave + item + (item >> 5)) & (NW - 1);
+    const int rw = row_group(wave, NW);  // this wave's 32 rows of the q-block
     const int q0 = qb * QB;
     const bool q_ragged = q0 + QB > p.q_len;
 

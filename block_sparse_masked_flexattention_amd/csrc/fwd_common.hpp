@@ -96,6 +96,19 @@ __device__ inline void wg_to_tile(int n_qb, int& bh, int& qb) {
   xcd_item(gridDim.x, n_qb, w & 7, w >> 3, bh, qb);
 }
 
+// The 32-row group a wave takes in a work-group of nw waves (a power of
+// two), rotated by the work-group's item.  The waves of a work-group run
+// their steps together (one barrier per step), and near the diagonal or a
+// window edge the groups see unequal numbers of blocks per step; with wave w
+// of every resident work-group on the same SIMD, equal groups would stack
+// the same imbalance there.  The rotation differs between consecutive items
+// of an XCD and between items 32 apart, the neighbours on one CU under
+// either fill order.
+__device__ inline int row_group(int wave, int nw) {
+  const int item = (int)(blockIdx.x >> 3);
+  return (wave + item + (item >> 5)) & (nw - 1);
+}
+
 // Keys visible from query row qi, as one interval [lo, hi] (empty when
 // lo > hi), already clipped to the key range.
 template <int MASK, typename P>
