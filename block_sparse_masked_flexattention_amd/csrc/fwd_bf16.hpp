@@ -194,7 +194,10 @@ struct Bf16Fwd {
     int bh, qb;
     wg_to_tile(p.n_qb, bh, qb);
     const int h = bh % p.H;
-    const int rw = row_group(wave, NW);  // this wave's 32 rows of the q-block
+    // this wave's 32 rows of the q-block: rotated under the sliding window,
+    // where every q-block has the same uneven per-step block counts (under
+    // the prefix-or-causal mask the rotation measured about 1% slower)
+    const int rw = MASK == FLEX_MASK_SLIDING_WINDOW ? row_group(wave, NW) : wave;
     const int q0 = qb * QB;
     const bool q_ragged = q0 + QB > p.q_len;
 
