@@ -38,6 +38,10 @@ def _both(cfg):
      ("sliding_window", dict(B=1, H=2, q_len=333, kv_len=333))),
     (("causal_rel_bias", dict(B=1, H=8, q_len=700, kv_len=700)),
      ("long_causal_d128", dict(B=1, H=2, q_len=200, kv_len=200))),
+    # fp32 inputs (the vector-ALU kernels), value head dims unlike the key's
+    (("prefix_causal", dict(B=1, H=2, q_len=520, kv_len=520, dtype="fp32", dv=128,
+                            mask={"kind": "prefix_causal", "prefix": 200})),
+     ("long_causal_d128", dict(B=1, H=1, q_len=150, kv_len=150, dtype="fp32", dv=64))),
 ])
 def test_noalloc_backward_equals_workspace_backward(first, second):
     for name, over in (first, second):
