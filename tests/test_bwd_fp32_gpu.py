@@ -221,6 +221,37 @@ def test_fp32_empty_ranges():
     assert bool(torch.all(dk == 0)) and bool(torch.all(dv == 0))
 
 
+def test_fp32_empty_ranges_value_head_dim():
+    """As above with value head dims unlike the key's.  kv_len = 0 with
+    D = 128, Dv = 64: the forward writes out 0 and lse -inf, dq is 0;
+    q_len = 0 with D = 64, Dv = 128: dk (64 wide) and dv (128 wide) are 0."""
+    B, H = 1, 2
+    q = torch.randn(B, H, 70, 128, device=DEV)
+    ek, ev = torch.zeros(B, H, 0, 128, device=DEV), torch.zeros(B, H, 0, 64, device=DEV)
+    bm = fa.build_block_mask({"kind": "causal"}, 70, 0, 64, 64, device=DEV)
+    bmt = fa.build_block_mask_t({"kind": "causal"}, 70, 0, 64, 64, device=DEV)
+    out = torch.full((B, H, 70, 64), 7.0, device=DEV)
+    lse = torch.zeros(B, H, 70, device=DEV)
+    fa.fwd(q, ek, ev, bm, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 0)) and bool(torch.all(torch.isneginf(lse)))
+    dout = torch.randn(B, H, 70, 64, device=DEV)
+    dq, dk, dv = fa.bwd(q, ek, ev, out, dout, lse, bm, bmt)
+    torch.cuda.synchronize()
+    assert dk.numel() == 0 and dv.numel() == 0 and dq.shape == q.shape
+    assert bool(torch.all(dq == 0))
+    k = torch.randn(B, H, 150, 64, device=DEV)
+    v = torch.randn(B, H, 150, 128, device=DEV)
+    eq, eo = torch.zeros(B, H, 0, 64, device=DEV), torch.zeros(B, H, 0, 128, device=DEV)
+    bm = fa.build_block_mask({"kind": "noop"}, 0, 150, 128, 128, device=DEV)
+    bmt = fa.build_block_mask_t({"kind": "noop"}, 0, 150, 128, 128, device=DEV)
+    dk = torch.full((B, H, 150, 64), 7.0, device=DEV)
+    dv = torch.full((B, H, 150, 128), 7.0, device=DEV)
+    fa.bwd(eq, k, v, eo, eo, torch.zeros(B, H, 0, device=DEV), bm, bmt, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert bool(torch.all(dk == 0)) and bool(torch.all(dv == 0))
+
+
 def test_fp32_fully_masked_rows_and_keys():
     """window_min = 5 hides every key from rows 0..4 and the last five keys
     from every row: those dq rows and dk / dv rows are exactly 0."""
