@@ -263,3 +263,13 @@ def test_fp32_fully_masked_rows_and_keys():
     dq, dk, dv = run(cfg, cfg["mask"], q, k, v, dout)
     assert np.all(dq[:, :, :5] == 0.0)
     assert np.all(dk[:, :, -5:] == 0.0) and np.all(dv[:, :, -5:] == 0.0)
+
+
+@pytest.mark.parametrize("seed", range(500, 516))
+def test_fp32_random_case(seed):
+    """Seeded random draws (mask kind and parameters, score modification, head
+    dims, tile shape, ragged and unequal lengths, gradient dtype, lse
+    gradient) as in the bf16 sweep, with fp32 inputs."""
+    from test_bwd_random_gpu import _case as draw
+    over, grad_dtype, with_dlse = draw(seed)
+    _case("prefix_causal", over, grad_dtype=grad_dtype, with_dlse=with_dlse)

@@ -1,8 +1,9 @@
-"""Seeded random sweep of the bf16 forward against the fp64 oracle: mask
-kind and its parameters, score modification, head dims, tile shape, ragged
-and unequal lengths, output dtype and the subtiled rescale are drawn per
-case, so that combinations the hand-picked cases miss still meet the bar
-(max-abs 1e-2 on the output, 1e-3 on the log-sum-exp; see tests/parity.py)."""
+"""Seeded random sweep of the forward against the fp64 oracle: mask kind and
+its parameters, score modification, head dims, tile shape, ragged and unequal
+lengths, output dtype and the subtiled rescale are drawn per case, so that
+combinations the hand-picked cases miss still meet the bar (bf16 inputs:
+max-abs 1e-2 on the output, 1e-3 on the log-sum-exp; fp32 inputs: the fp32
+bar of tests/parity.py on both)."""
 import numpy as np
 import pytest
 import torch
@@ -38,15 +39,28 @@ def _case(seed):
     return over, out_dtype, bool(r.integers(4) == 0)
 
 
-@pytest.mark.parametrize("seed", range(64))
-def test_random_case(seed):
-    over, out_dtype, sub = _case(seed)
+def _run_case(seed, over, out_dtype, sub, in_dtype):
     cfg = workload("prefix_causal", **over)
+    cfg["dtype"] = in_dtype
     cfg["mask"] = with_doc_ids(cfg)
     q, k, v = make_inputs(cfg)
     out, lse, _ = run_gpu(dict(cfg, mask=with_doc_ids(cfg, torch.device("cuda:0"))), q, k, v,
                           out_dtype=out_dtype, lse=True, use_subtiling=sub)
     ref_out, ref_lse = oracle_rows(cfg, q, k, v)
-    compare(out.reshape(-1, cfg["dv"]), lse.reshape(-1), ref_out, ref_lse, "bf16",
+    compare(out.reshape(-1, cfg["dv"]), lse.reshape(-1), ref_out, ref_lse, in_dtype,
             "bf16" if out_dtype == torch.bfloat16 else "fp32",
             what="seed %d: %s" % (seed, {k_: over[k_] for k_ in ("q_len", "kv_len", "d", "dv", "q_block", "kv_block", "mask", "score")}))
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_case(seed):
+    over, out_dtype, sub = _case(seed)
+    _run_case(seed, over, out_dtype, sub, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(1000, 1024))
+def test_random_case_fp32(seed):
+    """The same draws with fp32 inputs (the fp32 kernel; the subtiling flag
+    selects the same arithmetic there)."""
+    over, out_dtype, sub = _case(seed)
+    _run_case(seed, over, out_dtype, sub, "fp32")
