@@ -258,7 +258,11 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
   // document kinds, its columns); their verdicts meet through shuffles
   constexpr int kLanes = 8;
   constexpr int kTiles = kThreads / kLanes;  // tiles per pass over the column
+  // the first pass keeps each tile's class here for the second, when the
+  // column has at most kMaxCached q-blocks; longer columns classify twice
+  constexpr int kMaxCached = 4096;
   __shared__ int scratch[kWaves];
+  __shared__ unsigned char cls[kMaxCached];
   const int kb = blockIdx.x;
   const int nq = p.n_qb;
   const size_t col = (size_t)kb * nq;
@@ -267,13 +271,19 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
   const int c_last = min(c_end, p.kv_len - 1);  // c0 <= kv_len - 1 since kb < n_kb
   const int sub = (int)threadIdx.x % kLanes;
   const bool doc = p.kind == FLEX_MASK_DOCUMENT || p.kind == FLEX_MASK_DOCUMENT_CAUSAL;
+  const bool cached = nq <= kMaxCached;
   int n_part = 0, n_full = 0;
   for (int pass = 0; pass < 2; ++pass) {
     int seen_part = 0, seen_full = 0;
     for (int q00 = 0; q00 < nq; q00 += kTiles) {
       const int qb = q00 + (int)threadIdx.x / kLanes;
       int all = 1, any = 0;
-      if (qb < nq) {
+      if (pass == 1 && cached) {
+        // (written in pass 0 before a barrier of its scans)
+        const int c0c = qb < nq ? cls[qb] : 0;
+        all = c0c == 2;
+        any = c0c != 0;
+      } else if (qb < nq) {
         const int r0 = qb * p.q_block;
         const int r1 = min(r0 + p.q_block, p.q_len);
         all = r0 + p.q_block <= p.q_len && c_end < p.kv_len;
@@ -294,13 +304,16 @@ __global__ __launch_bounds__(kThreads) void build_block_mask_t_kernel(MaskBuildP
           }
         }
       }
+      if (pass == 0 || !cached) {
 #pragma unroll
-      for (int o = 1; o < kLanes; o <<= 1) {
-        all &= __shfl_xor(all, o);
-        any |= __shfl_xor(any, o);
+        for (int o = 1; o < kLanes; o <<= 1) {
+          all &= __shfl_xor(all, o);
+          any |= __shfl_xor(any, o);
+        }
       }
       // one flag per tile, on its first lane: thread order is q-block order
       const int c = (qb < nq && sub == 0) ? (all ? 2 : (any ? 1 : 0)) : 0;
+      if (pass == 0 && cached && qb < nq && sub == 0) cls[qb] = (unsigned char)c;
       int tp, tf;
       const int bp = seen_part + block_prefix(c == 1, scratch, &tp);
       const int bf = seen_full + block_prefix(c == 2, scratch, &tf);
